@@ -1,0 +1,153 @@
+/*
+ * kvq.h -- C ABI of libkvq.so: KV-cache compress -> quantise -> paged store on MI355X
+ * (gfx950), plus the matching page dequant and the once-per-step full -> SWA slot
+ * translation.
+ *
+ * Sources (web pages the operations follow):
+ *  [P1] "sglang, DeepSeek V4.1 Paged KV Cache: V41 and FP4 formats" (sglang PR #39123
+ *       analysis): section 1 (V41 / V41_FP4 layouts, PagedKV page/row/scale-row
+ *       addressing, store_row with the ue8m0 exponent taken from the amax bits),
+ *       section 2 (c1 / c2 compressor writes templated on the layout, FP4 quantised
+ *       once), section 4 (dequant of pages into a bf16 workspace), section 5 (the pool
+ *       reports bytes per token and bytes per page instead of a hard-coded 584).
+ *  [P2] "SGLang: DeepSeek-v4 SWA index translation hoisting" (sglang PR #34890
+ *       analysis): sections 1-2 (translate out_cache_loc once per step into a
+ *       preallocated int32 buffer; zero the tail; refuse when the batch is larger).
+ *  [P3] "DeepSeek V4 Sparse FP8 Compressor kernel optimisation with CuteDSL" (vLLM PR
+ *       #44161 analysis): sections 1-3 (per-channel online-softmax pooling of each
+ *       ratio-r window of fp32 rows, RoPE, per-32 absmax fp8 scale).
+ *
+ * Common rules for every entry point
+ *  - All array arguments are DEVICE pointers owned by the caller; the library keeps no
+ *    reference after the call returns.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *    asynchronously on it; no call allocates, frees or synchronises, so every call can
+ *    be captured into a hipGraph.
+ *  - Calls are stateless and thread-safe.  Two calls that write the same pool slots or
+ *    output rows concurrently race (the caller orders them with streams/events).
+ *  - Host-side validation only: arguments are checked before any launch and an error
+ *    returns without enqueuing anything.  Device data is not validated, except that a
+ *    row whose slot is outside [0, num_pages*64) or whose position is outside
+ *    [0, max_pos) is skipped (nothing is written for it).  Duplicate slots within one
+ *    call are a caller error (which row wins is unspecified).
+ *  - n == 0 (or R == 0, P == 0) returns KVQ_OK without launching, except
+ *    kv_translate_slots, which still zeroes out[0:cap].
+ *  - Inputs must be finite; non-finite values give unspecified codes.
+ *
+ * Pool layout (PagedKV, page size 64 tokens, [P1] section 1): the pool is num_pages
+ * pages of kvq_page_bytes(layout) bytes each, contiguous from `pool`.  Slot s lives in
+ * page s >> 6, row s & 63.  A page holds 64 code rows followed by 64 scale rows:
+ *   code row  at pool + page*PB + row*CR          (CR = kvq_code_row_bytes)
+ *   scale row at pool + page*PB + 64*CR + row*SR  (SR = kvq_scale_row_bytes)
+ * V41:     CR = 512 (e4m3 code of channel c at byte c), SR = 16 (ue8m0 byte b scales
+ *          channels 32b..32b+31): 528 B/token, PB = 33792.
+ * V41_FP4: CR = 256 (channel 2j in the low nibble of byte j, 2j+1 in the high nibble),
+ *          SR = 32 (16 e4m3 scale bytes, then 16 zero pad bytes): 288 B/token,
+ *          PB = 18432.
+ *
+ * Row encoding (per 32-channel block of bf16 values v, amax = max |v|):
+ *  V41:     k = smallest integer >= -127 with amax <= 448 * 2^k; scale byte k + 127;
+ *           code = e4m3fn(v * 2^-k), round to nearest even, sign kept.
+ *  V41_FP4: s = e4m3fn(fl32(amax / 6)) rounded to nearest even, held at 448;
+ *           code = e2m1(fl32(v / s)), round to nearest even, magnitudes above 6 held at
+ *           6, sign kept; all codes 0 when s == 0.
+ */
+#ifndef KVQ_H_
+#define KVQ_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes -------------------------------------------------------------- */
+#define KVQ_OK 0
+#define KVQ_EINVAL (-1)    /* null pointer with work to do, ld < 512, misaligned
+                              pointer or stride, negative size, max_pos <= 0       */
+#define KVQ_ELAYOUT (-2)   /* layout id is not KVQ_LAYOUT_V41 / KVQ_LAYOUT_V41_FP4 */
+#define KVQ_ERATIO (-3)    /* compression ratio not built (supported: 1, 2, 4, 128) */
+#define KVQ_ECAPACITY (-4) /* kv_translate_slots with n > cap; nothing enqueued   */
+#define KVQ_ELAUNCH (-5)   /* the HIP runtime rejected the kernel launch          */
+
+/* ---- layout ids ---------------------------------------------------------------- */
+#define KVQ_LAYOUT_V41 1     /* fp8 e4m3 codes + ue8m0 scale per 32: 528 B/token     */
+#define KVQ_LAYOUT_V41_FP4 2 /* e2m1 codes + e4m3 scale per 32 (+pad): 288 B/token  */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* kvq_status_string(int status);
+
+/* Layout queries ([P1] sections 1 and 5).  Each returns the byte count, or
+ * KVQ_ELAYOUT for an unknown layout. */
+int64_t kvq_bytes_per_token(int32_t layout);  /* 528 | 288                     */
+int64_t kvq_page_bytes(int32_t layout);       /* 64 * bytes per token         */
+int64_t kvq_code_row_bytes(int32_t layout);   /* 512 | 256                     */
+int64_t kvq_scale_row_bytes(int32_t layout);  /* 16 | 32                       */
+
+/* kv_store -- quantise n bf16 K rows and write them at their slots ([P1] section 1,
+ * store_row; the plain "store" kernel of the latency table).
+ *   pool       device, num_pages * kvq_page_bytes(layout) bytes, 16-byte aligned
+ *   k          device bf16 bits, row i at k + i*ld, 512 channels used; 16-byte aligned
+ *   ld         row stride in elements, >= 512 and a multiple of 8
+ *   slots      device int32[n]
+ * Returns KVQ_OK or KVQ_EINVAL / KVQ_ELAYOUT / KVQ_ELAUNCH. */
+int kv_store(int32_t layout, void* pool, int64_t num_pages, const uint16_t* k, int64_t ld,
+             const int32_t* slots, int64_t n, void* stream);
+
+/* kv_store_rope -- as kv_store, but first rotates the last 64 channels of each row by
+ * its position (NeoX half rotation: channel 448+i pairs with 480+i, i < 32) and rounds
+ * the rotated values to bf16 ([P1] latency table "store + RoPE"; [P3] section 3).
+ *   pos        device int32[n], positions; rows with pos outside [0, max_pos) skipped
+ *   cos_sin    device fp32[max_pos][64]: cos of the 32 angles of a position, then their
+ *              sin; 16-byte aligned.  Built by the caller (a RoPE table is model data).
+ *   max_pos    rows in cos_sin, > 0
+ * The rotation is o1 = x1*c - x2*s, o2 = x2*c + x1*s with every product and sum
+ * rounded to fp32 separately (no fused multiply-add), so results are deterministic. */
+int kv_store_rope(int32_t layout, void* pool, int64_t num_pages, const uint16_t* k,
+                  int64_t ld, const int32_t* pos, const float* cos_sin, int64_t max_pos,
+                  const int32_t* slots, int64_t n, void* stream);
+
+/* kv_compress_store -- the c1 / C4A / C128A compressors ([P3] sections 1-3; [P1]
+ * section 2).  Output row i pools input rows [i*ratio, i*ratio + ratio) channel by
+ * channel: weights are the softmax over the window of score[.][c], the pooled value is
+ * the weighted sum of kv[.][c] (computed in fp32 with an online max, then rounded to
+ * bf16); then RoPE at pos[i] as in kv_store_rope; then quantise and store at slots[i].
+ * ratio 1 is the identity (score is not read).
+ *   kv, score  device fp32, row j at base + j*ld, R*ratio rows; 16-byte aligned
+ *   ld         row stride in elements, >= 512 and a multiple of 4
+ *   ratio      1, 2, 4 or 128 (others: KVQ_ERATIO)
+ *   pos, slots device int32[R]
+ * Compressed codes may differ from an exact (float64) evaluation by at most one code
+ * step where the fp32 pooled value rounds to a different bf16. */
+int kv_compress_store(int32_t layout, void* pool, int64_t num_pages, const float* kv,
+                      const float* score, int64_t ld, int32_t ratio, const int32_t* pos,
+                      const float* cos_sin, int64_t max_pos, const int32_t* slots,
+                      int64_t R, void* stream);
+
+/* kv_dequant -- turn whole pages back into a bf16 workspace ([P1] section 4).
+ * For p < P and each of the 64 rows r of page page_ids[p]:
+ *   out[(p*64 + r)*512 + c] = bf16_rne(fp32(decode(code) * decode(scale)))
+ * A NaN code or scale gives 0x7FC0.  A page id outside [0, num_pages) leaves its 64
+ * output rows untouched.
+ *   page_ids   device int32[P]
+ *   out        device bf16 bits, [P*64][512], 16-byte aligned */
+int kv_dequant(int32_t layout, const void* pool, int64_t num_pages, const int32_t* page_ids,
+               int64_t P, uint16_t* out, void* stream);
+
+/* kv_translate_slots -- full-pool -> SWA-pool slot translation, done once per step into
+ * a preallocated buffer ([P2] sections 1-2):
+ *   out[i] = table[full_loc[i]] for i < n (-1 when full_loc[i] is outside
+ *            [0, table_len)), out[i] = 0 for n <= i < cap.
+ * n > cap returns KVQ_ECAPACITY and enqueues nothing; the caller then translates into a
+ * buffer of its own of n entries (the eager, still once-per-step, fallback).
+ *   table      device int32[table_len]
+ *   full_loc   device int32[n]
+ *   out        device int32[cap] */
+int kv_translate_slots(const int32_t* table, int64_t table_len, const int32_t* full_loc,
+                       int64_t n, int32_t* out, int64_t cap, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H_ */

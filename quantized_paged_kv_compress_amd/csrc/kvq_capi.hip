@@ -1,0 +1,198 @@
+// kvq_capi.hip -- the C ABI of libkvq.so: host-side validation and kernel launches.
+//
+// Every entry point validates its arguments on the host, then enqueues kernels on the
+// caller's stream with hipLaunchKernel (whose return code reports a rejected launch
+// without touching the process-wide last-error state).  Nothing allocates, frees or
+// synchronises.  Declarations, argument meaning and error behaviour: include/kvq.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <tuple>
+
+#include "kvq.h"
+#include "kvq_kernels.hpp"
+#include "kvq_layout.hpp"
+
+namespace {
+
+using kvq::Layout;
+
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool known_layout(int32_t layout) {
+    return layout == KVQ_LAYOUT_V41 || layout == KVQ_LAYOUT_V41_FP4;
+}
+
+template <typename... KArgs, typename... Args>
+int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, void* stream, Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+    std::tuple<KArgs...> vals(static_cast<KArgs>(args)...);
+    void* ptrs[sizeof...(KArgs)];
+    std::apply([&](auto&... a) {
+        int j = 0;
+        ((ptrs[j++] = const_cast<void*>(static_cast<const void*>(&a))), ...);
+    }, vals);
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : KVQ_ELAUNCH;
+}
+
+unsigned blocks_for(int64_t rows, int per_block) {
+    return static_cast<unsigned>((rows + per_block - 1) / per_block);
+}
+
+template <Layout L>
+int store_impl(bool rope, void* pool, int64_t num_pages, const uint16_t* k, int64_t ld,
+               const int32_t* pos, const float* cos_sin, int64_t max_pos, const int32_t* slots,
+               int64_t n, void* stream) {
+    const dim3 grid(blocks_for(n, kvq::kRowsPerBlock)), block(kvq::kWave * kvq::kRowsPerBlock);
+    const int64_t nslots = num_pages << kvq::kPageBits;
+    auto* p = static_cast<uint8_t*>(pool);
+    if (rope)
+        return launch(kvq::store_kernel<L, true>, grid, block, stream, p, nslots, k, ld, pos,
+                      cos_sin, max_pos, slots, n);
+    return launch(kvq::store_kernel<L, false>, grid, block, stream, p, nslots, k, ld, pos,
+                  cos_sin, max_pos, slots, n);
+}
+
+template <Layout L, int kRatio>
+int compress_short(void* pool, int64_t num_pages, const float* kv, const float* score, int64_t ld,
+                   const int32_t* pos, const float* cos_sin, int64_t max_pos,
+                   const int32_t* slots, int64_t R, void* stream) {
+    return launch(kvq::compress_short_kernel<L, kRatio>, dim3(blocks_for(R, kvq::kRowsPerBlock)),
+                  dim3(kvq::kWave * kvq::kRowsPerBlock), stream, static_cast<uint8_t*>(pool),
+                  num_pages << kvq::kPageBits, kv, score, ld, pos, cos_sin, max_pos, slots, R);
+}
+
+template <Layout L, int kRatio, int kWaves, int kChunk>
+int compress_long(void* pool, int64_t num_pages, const float* kv, const float* score, int64_t ld,
+                  const int32_t* pos, const float* cos_sin, int64_t max_pos,
+                  const int32_t* slots, int64_t R, void* stream) {
+    return launch(kvq::compress_long_kernel<L, kRatio, kWaves, kChunk>, dim3(static_cast<unsigned>(R)),
+                  dim3(kvq::kWave * kWaves), stream, static_cast<uint8_t*>(pool),
+                  num_pages << kvq::kPageBits, kv, score, ld, pos, cos_sin, max_pos, slots, R);
+}
+
+template <Layout L>
+int compress_dispatch(int32_t ratio, void* pool, int64_t num_pages, const float* kv,
+                      const float* score, int64_t ld, const int32_t* pos, const float* cos_sin,
+                      int64_t max_pos, const int32_t* slots, int64_t R, void* stream) {
+    switch (ratio) {
+        case 1: return compress_short<L, 1>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 2: return compress_short<L, 2>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 4: return compress_short<L, 4>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 128: return compress_long<L, 128, 4, 4>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
+        default: return KVQ_ERATIO;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_string(int status) {
+    switch (status) {
+        case KVQ_OK: return "ok";
+        case KVQ_EINVAL: return "invalid argument (null pointer, stride, alignment or size)";
+        case KVQ_ELAYOUT: return "unknown layout id";
+        case KVQ_ERATIO: return "compression ratio not supported (1, 2, 4, 128)";
+        case KVQ_ECAPACITY: return "more slots than the translation buffer holds";
+        case KVQ_ELAUNCH: return "kernel launch rejected by the HIP runtime";
+        default: return "unknown status";
+    }
+}
+
+int64_t kvq_code_row_bytes(int32_t layout) {
+    if (layout == KVQ_LAYOUT_V41) return kvq::LayoutTraits<Layout::V41>::kCodeRowBytes;
+    if (layout == KVQ_LAYOUT_V41_FP4) return kvq::LayoutTraits<Layout::V41_FP4>::kCodeRowBytes;
+    return KVQ_ELAYOUT;
+}
+
+int64_t kvq_scale_row_bytes(int32_t layout) {
+    if (layout == KVQ_LAYOUT_V41) return kvq::LayoutTraits<Layout::V41>::kScaleRowBytes;
+    if (layout == KVQ_LAYOUT_V41_FP4) return kvq::LayoutTraits<Layout::V41_FP4>::kScaleRowBytes;
+    return KVQ_ELAYOUT;
+}
+
+int64_t kvq_bytes_per_token(int32_t layout) {
+    if (layout == KVQ_LAYOUT_V41) return kvq::kTokenBytes<Layout::V41>;
+    if (layout == KVQ_LAYOUT_V41_FP4) return kvq::kTokenBytes<Layout::V41_FP4>;
+    return KVQ_ELAYOUT;
+}
+
+int64_t kvq_page_bytes(int32_t layout) {
+    if (layout == KVQ_LAYOUT_V41) return kvq::PagedKV<Layout::V41, kvq::kPageBits>::kPageBytes;
+    if (layout == KVQ_LAYOUT_V41_FP4) return kvq::PagedKV<Layout::V41_FP4, kvq::kPageBits>::kPageBytes;
+    return KVQ_ELAYOUT;
+}
+
+static int store_common(bool rope, int32_t layout, void* pool, int64_t num_pages, const uint16_t* k,
+                        int64_t ld, const int32_t* pos, const float* cos_sin, int64_t max_pos,
+                        const int32_t* slots, int64_t n, void* stream) {
+    if (!known_layout(layout)) return KVQ_ELAYOUT;
+    if (n < 0 || n > kMaxRows || num_pages < 0) return KVQ_EINVAL;
+    if (rope && max_pos <= 0) return KVQ_EINVAL;
+    if (n == 0) return KVQ_OK;
+    if (!pool || !k || !slots || (rope && (!pos || !cos_sin))) return KVQ_EINVAL;
+    if (ld < kvq::kHeadDim || ld % 8 != 0) return KVQ_EINVAL;
+    if (!aligned16(pool) || !aligned16(k) || (rope && !aligned16(cos_sin))) return KVQ_EINVAL;
+    if (layout == KVQ_LAYOUT_V41)
+        return store_impl<Layout::V41>(rope, pool, num_pages, k, ld, pos, cos_sin, max_pos, slots, n, stream);
+    return store_impl<Layout::V41_FP4>(rope, pool, num_pages, k, ld, pos, cos_sin, max_pos, slots, n, stream);
+}
+
+int kv_store(int32_t layout, void* pool, int64_t num_pages, const uint16_t* k, int64_t ld,
+             const int32_t* slots, int64_t n, void* stream) {
+    return store_common(false, layout, pool, num_pages, k, ld, nullptr, nullptr, 1, slots, n, stream);
+}
+
+int kv_store_rope(int32_t layout, void* pool, int64_t num_pages, const uint16_t* k, int64_t ld,
+                  const int32_t* pos, const float* cos_sin, int64_t max_pos, const int32_t* slots,
+                  int64_t n, void* stream) {
+    return store_common(true, layout, pool, num_pages, k, ld, pos, cos_sin, max_pos, slots, n, stream);
+}
+
+int kv_compress_store(int32_t layout, void* pool, int64_t num_pages, const float* kv,
+                      const float* score, int64_t ld, int32_t ratio, const int32_t* pos,
+                      const float* cos_sin, int64_t max_pos, const int32_t* slots, int64_t R,
+                      void* stream) {
+    if (!known_layout(layout)) return KVQ_ELAYOUT;
+    if (ratio != 1 && ratio != 2 && ratio != 4 && ratio != 128) return KVQ_ERATIO;
+    if (R < 0 || R > kMaxRows || num_pages < 0 || max_pos <= 0) return KVQ_EINVAL;
+    if (R == 0) return KVQ_OK;
+    if (!pool || !kv || (ratio > 1 && !score) || !pos || !cos_sin || !slots) return KVQ_EINVAL;
+    if (ld < kvq::kHeadDim || ld % 4 != 0) return KVQ_EINVAL;
+    if (!aligned16(pool) || !aligned16(kv) || (ratio > 1 && !aligned16(score)) || !aligned16(cos_sin))
+        return KVQ_EINVAL;
+    if (layout == KVQ_LAYOUT_V41)
+        return compress_dispatch<Layout::V41>(ratio, pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
+    return compress_dispatch<Layout::V41_FP4>(ratio, pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
+}
+
+int kv_dequant(int32_t layout, const void* pool, int64_t num_pages, const int32_t* page_ids,
+               int64_t P, uint16_t* out, void* stream) {
+    if (!known_layout(layout)) return KVQ_ELAYOUT;
+    if (P < 0 || P > (kMaxRows >> kvq::kPageBits) || num_pages < 0) return KVQ_EINVAL;
+    if (P == 0) return KVQ_OK;
+    if (!pool || !page_ids || !out) return KVQ_EINVAL;
+    if (!aligned16(pool) || !aligned16(out)) return KVQ_EINVAL;
+    const dim3 grid(blocks_for(P << kvq::kPageBits, kvq::kRowsPerBlock)), block(kvq::kWave * kvq::kRowsPerBlock);
+    const auto* p = static_cast<const uint8_t*>(pool);
+    if (layout == KVQ_LAYOUT_V41)
+        return launch(kvq::dequant_kernel<Layout::V41>, grid, block, stream, p, num_pages, page_ids, P, out);
+    return launch(kvq::dequant_kernel<Layout::V41_FP4>, grid, block, stream, p, num_pages, page_ids, P, out);
+}
+
+int kv_translate_slots(const int32_t* table, int64_t table_len, const int32_t* full_loc, int64_t n,
+                       int32_t* out, int64_t cap, void* stream) {
+    if (n < 0 || cap < 0 || table_len < 0 || cap > kMaxRows) return KVQ_EINVAL;
+    if (n > cap) return KVQ_ECAPACITY;
+    if (cap == 0) return KVQ_OK;
+    if (!out || (n > 0 && (!table || !full_loc))) return KVQ_EINVAL;
+    return launch(kvq::translate_kernel, dim3(blocks_for(cap, 256)), dim3(256), stream, table, table_len,
+                  full_loc, n, out, cap);
+}
+
+}  // extern "C"

@@ -1,0 +1,167 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every entry
+point that include/kvq.h declares, reports the layout sizes, and rejects bad arguments
+before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from helpers import FP4, V41
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    import quantized_paged_kv_compress_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from quantized_paged_kv_compress_amd import _build
+        _build.build()
+    m.load_library()
+    return m
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("kv_store", "kv_store_rope", "kv_compress_store", "kv_dequant",
+                 "kv_translate_slots", "kvq_bytes_per_token", "kvq_page_bytes"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(kvq):
+    lib = ctypes.CDLL(kvq.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_layout_queries(kvq, orc):
+    for lay in (V41, FP4):
+        assert kvq.bytes_per_token(lay) == orc.bytes_per_token(lay)
+        assert kvq.page_bytes(lay) == orc.page_bytes(lay)
+        assert kvq.code_row_bytes(lay) == orc.code_row_bytes(lay)
+        assert kvq.scale_row_bytes(lay) == orc.scale_row_bytes(lay)
+    assert kvq.bytes_per_token(V41) == 528 and kvq.bytes_per_token(FP4) == 288
+    assert kvq.page_bytes(V41) == 33792 and kvq.page_bytes(FP4) == 18432
+    assert kvq.bytes_per_token(3) == kvq.KVQ_ELAYOUT
+    assert kvq.page_bytes(0) == kvq.KVQ_ELAYOUT
+
+
+def test_status_strings(kvq):
+    lib = kvq.load_library()
+    for st in range(-5, 1):
+        assert lib.kvq_status_string(st)
+    assert b"unknown" in lib.kvq_status_string(-99)
+
+
+# Fake, 16-byte aligned addresses: every call below must be rejected (or be a no-op)
+# on the host, so none of them is ever dereferenced.
+A = 0x10000
+B = 0x20000
+C = 0x30000
+
+
+def test_store_argument_checks(kvq):
+    L = kvq.load_library()
+    assert L.kv_store(7, A, 4, B, 512, C, 10, None) == kvq.KVQ_ELAYOUT
+    assert L.kv_store(V41, A, 4, B, 512, C, 0, None) == kvq.KVQ_OK       # nothing to do
+    assert L.kv_store(V41, None, 4, B, 512, C, 1, None) == kvq.KVQ_EINVAL
+    assert L.kv_store(V41, A, 4, None, 512, C, 1, None) == kvq.KVQ_EINVAL
+    assert L.kv_store(V41, A, 4, B, 512, None, 1, None) == kvq.KVQ_EINVAL
+    assert L.kv_store(V41, A, 4, B, 511, C, 1, None) == kvq.KVQ_EINVAL   # ld < 512
+    assert L.kv_store(V41, A, 4, B, 516, C, 1, None) == kvq.KVQ_EINVAL   # ld % 8
+    assert L.kv_store(V41, A + 8, 4, B, 512, C, 1, None) == kvq.KVQ_EINVAL  # pool align
+    assert L.kv_store(FP4, A, 4, B + 2, 512, C, 1, None) == kvq.KVQ_EINVAL  # k align
+    assert L.kv_store(V41, A, -1, B, 512, C, 1, None) == kvq.KVQ_EINVAL
+    assert L.kv_store(V41, A, 4, B, 512, C, -3, None) == kvq.KVQ_EINVAL
+    assert L.kv_store(V41, A, 4, B, 512, C, 1 << 31, None) == kvq.KVQ_EINVAL
+
+
+def test_store_rope_argument_checks(kvq):
+    L = kvq.load_library()
+    assert L.kv_store_rope(V41, A, 4, B, 512, C, A, 0, C, 1, None) == kvq.KVQ_EINVAL  # max_pos
+    assert L.kv_store_rope(V41, A, 4, B, 512, None, A, 10, C, 1, None) == kvq.KVQ_EINVAL
+    assert L.kv_store_rope(V41, A, 4, B, 512, C, None, 10, C, 1, None) == kvq.KVQ_EINVAL
+    assert L.kv_store_rope(V41, A, 4, B, 512, C, A + 4, 10, C, 1, None) == kvq.KVQ_EINVAL
+    assert L.kv_store_rope(9, A, 4, B, 512, C, A, 10, C, 1, None) == kvq.KVQ_ELAYOUT
+    assert L.kv_store_rope(FP4, A, 4, B, 512, C, A, 10, C, 0, None) == kvq.KVQ_OK
+
+
+def test_compress_argument_checks(kvq):
+    L = kvq.load_library()
+    ok = (V41, A, 4, B, C, 512, 4, A, B, 10, C, 5, None)
+    def call(**kw):
+        names = ["layout", "pool", "num_pages", "kv", "score", "ld", "ratio", "pos", "cs",
+                 "max_pos", "slots", "R", "stream"]
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return L.kv_compress_store(*[args[n] for n in names])
+    for r in (0, 3, 5, 8, 64, 129, -4):
+        assert call(ratio=r) == kvq.KVQ_ERATIO
+    assert call(layout=0) == kvq.KVQ_ELAYOUT
+    assert call(R=0) == kvq.KVQ_OK
+    assert call(score=None) == kvq.KVQ_EINVAL
+    assert call(kv=None) == kvq.KVQ_EINVAL
+    assert call(pos=None) == kvq.KVQ_EINVAL
+    assert call(cs=None) == kvq.KVQ_EINVAL
+    assert call(slots=None) == kvq.KVQ_EINVAL
+    assert call(max_pos=0) == kvq.KVQ_EINVAL
+    assert call(ld=510) == kvq.KVQ_EINVAL
+    assert call(ld=514) == kvq.KVQ_EINVAL
+    assert call(kv=B + 4) == kvq.KVQ_EINVAL
+    assert call(score=C + 8) == kvq.KVQ_EINVAL
+    assert call(R=-1) == kvq.KVQ_EINVAL
+
+
+def test_dequant_and_translate_argument_checks(kvq):
+    L = kvq.load_library()
+    assert L.kv_dequant(5, A, 4, B, 1, C, None) == kvq.KVQ_ELAYOUT
+    assert L.kv_dequant(V41, A, 4, B, 0, C, None) == kvq.KVQ_OK
+    assert L.kv_dequant(V41, None, 4, B, 1, C, None) == kvq.KVQ_EINVAL
+    assert L.kv_dequant(V41, A, 4, None, 1, C, None) == kvq.KVQ_EINVAL
+    assert L.kv_dequant(V41, A, 4, B, 1, None, None) == kvq.KVQ_EINVAL
+    assert L.kv_dequant(FP4, A, 4, B, 1, C + 2, None) == kvq.KVQ_EINVAL
+    assert L.kv_dequant(FP4, A, 4, B, -1, C, None) == kvq.KVQ_EINVAL
+    # translate: n > cap is refused before anything else happens
+    assert L.kv_translate_slots(A, 100, B, 11, C, 10, None) == kvq.KVQ_ECAPACITY
+    assert L.kv_translate_slots(None, 0, None, 11, None, 10, None) == kvq.KVQ_ECAPACITY
+    assert L.kv_translate_slots(A, 100, B, 0, C, 0, None) == kvq.KVQ_OK
+    assert L.kv_translate_slots(A, 100, B, 5, None, 10, None) == kvq.KVQ_EINVAL
+    assert L.kv_translate_slots(None, 100, B, 5, C, 10, None) == kvq.KVQ_EINVAL
+    assert L.kv_translate_slots(A, -1, B, 5, C, 10, None) == kvq.KVQ_EINVAL
+    assert L.kv_translate_slots(A, 100, B, -1, C, 10, None) == kvq.KVQ_EINVAL
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    import quantized_paged_kv_compress_amd as m
+    monkeypatch.setattr(m, "_lib", None)
+    monkeypatch.setattr(m, "LIB_PATH", "/nonexistent/libkvq.so")
+    with pytest.raises(ImportError):
+        m.load_library()
+
+
+def test_binding_rejects_host_tensors(kvq):
+    import torch
+    pool = torch.zeros((2, kvq.page_bytes(V41)), dtype=torch.uint8)
+    k = torch.zeros((4, 512), dtype=torch.bfloat16)
+    slots = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        kvq.kv_store(pool, V41, k, slots)
+
+
+def test_product_path_does_not_reference_the_oracle():
+    """The library and its binding never import, load or call the CPU oracle."""
+    pkg = os.path.join(ROOT, "quantized_paged_kv_compress_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower() or f == "workloads.py" and "import oracle" not in text, f
+    for f in ("kvq.h",):
+        assert "oracle" not in open(os.path.join(ROOT, "include", f)).read().lower()
