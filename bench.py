@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Benchmark of the KV compress -> quantise -> paged-store path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic inputs already
+resident in HBM:
+  1. the mixed decode/prefill step (V41_FP4): full -> SWA slot translation of the
+     ragged batch's compressed rows, ratio-4 compression into the FP4 pool at the
+     translated slots, dequant of every touched page into a bf16 workspace;
+  2. C4A: 16384 output rows, ratio 4, fp32 kv/score [65536, 512], V41 pool;
+  3. C128A: 16384 output rows, ratio 128, fp32 kv/score [2097152, 512], V41 pool.
+Each step touches ~9.1 GB, far beyond the 256 MB last-level cache, so every kernel
+reads cold inputs.  `value` is compressed rows per second over the whole step; every
+kernel's HIP-event time, algorithmic bytes and fraction of the 8 TB/s HBM peak are in
+`kernels`; `roofline` is the dominant kernel (C128A).
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "compressed KV rows/sec + achieved HBM GB/s (% of MI355X peak), C4A & C128A"
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
+HEAD = 512
+PROFILE = os.path.join(ROOT, "profiles", "compress_c128a_v41_pmc.txt")
+KERNEL_SOURCES = ["csrc/kvq_capi.hip", "csrc/kvq_kernels.hpp", "csrc/kvq_device.hpp",
+                  "csrc/kvq_layout.hpp", "_build.py"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "quantized_paged_kv_compress_amd", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+# ---------------------------------------------------------------- algorithmic bytes
+# What the method must move, per launch: inputs read once, per-row metadata (position
+# 4 B, slot 4 B, the gathered 64-float cos/sin row 256 B), the stored row.
+def bytes_compress(R, ratio, token_bytes):
+    return R * (ratio * HEAD * 4 * 2 + 4 + 4 + 64 * 4 + token_bytes)
+
+
+def bytes_translate(n, cap):
+    return n * (4 + 4 + 4) + (cap - n) * 4
+
+
+def bytes_dequant(P, page_bytes):
+    return P * (4 + page_bytes + 64 * HEAD * 2)
+
+
+def read_traffic(duration_key_bytes):
+    """HBM bytes per C128A launch from the committed rocprofv3 PMC summary, scaled by
+    the copy-kernel calibration in the same file; None if the kernels changed since."""
+    if not os.path.exists(PROFILE):
+        return None
+    kv = {}
+    for line in open(PROFILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        if kv.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        copy_bytes = float(kv["copy_bytes_each_way"])
+        fs = copy_bytes / (float(kv["copy_FETCH_SIZE_KiB_per_dispatch"]) * 1024)
+        ws = copy_bytes / (float(kv["copy_WRITE_SIZE_KiB_per_dispatch"]) * 1024)
+        fetch = float(kv["FETCH_SIZE_KiB_per_dispatch"]) * 1024 * fs
+        write = float(kv["WRITE_SIZE_KiB_per_dispatch"]) * 1024 * ws
+        return {"bytes": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
+                "fetch_scale": fs, "write_scale": ws,
+                "ratio_to_algorithmic": (fetch + write) / duration_key_bytes}
+    except (KeyError, ValueError, ZeroDivisionError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this path runs on one GPU; every output row depends only on its own "
+              "window, so N GPUs would each run this same step on their own share "
+              "(no multi-GPU run is part of this build).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_paged_kv_compress_amd as kvq
+    from quantized_paged_kv_compress_amd import workloads as wl
+    if not os.path.exists(kvq.LIB_PATH):
+        from quantized_paged_kv_compress_amd import _build
+        _build.build()
+    kvq.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    def up(a):
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ------------------------------------------------------------ inputs (HBM resident)
+    t_gen = time.perf_counter()
+    cs_host = wl.rope_cos_sin()
+    cs = up(cs_host)
+    inputs = {}
+    cpu_rows_t = {}   # oracle seconds per workload (timed oracle calls only)
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.lib()
+    for name, seed, ratio in (("c4a", 3, 4), ("c128a", 4, 128)):
+        R = 16384
+        meta = wl.compressor_meta(seed, R)
+        kv = torch.empty((R * ratio, HEAD), dtype=torch.float32, device=dev)
+        sc = torch.empty_like(kv)
+        step = max(1, (1 << 26) // (HEAD * ratio))
+        orc_pool = None if args.no_cpu_baseline else oracle.new_pool(oracle.V41, meta["num_pages"])
+        t_orc = 0.0
+        for i0 in range(0, R, step):
+            n = min(step, R - i0)
+            a, b = wl.compressor_window(seed, ratio, i0, n)
+            kv[i0 * ratio:(i0 + n) * ratio].copy_(torch.from_numpy(a))
+            sc[i0 * ratio:(i0 + n) * ratio].copy_(torch.from_numpy(b))
+            if orc_pool is not None:   # CPU baseline: the oracle on the same rows, chunk by chunk
+                pos_c = np.ascontiguousarray(meta["pos"][i0:i0 + n])
+                slots_c = np.ascontiguousarray(meta["slots"][i0:i0 + n])
+                t = time.perf_counter()
+                oracle.kv_compress_store(oracle.V41, orc_pool, a, b, ratio, pos_c, cs_host, slots_c)
+                t_orc += time.perf_counter() - t
+        cpu_rows_t[name] = t_orc
+        del orc_pool
+        inputs[name] = dict(R=R, ratio=ratio, kv=kv, sc=sc, pos=up(meta["pos"]),
+                            slots=up(meta["slots"]), pool=kvq.new_pool(kvq.V41, meta["num_pages"]))
+        log(f"{name}: inputs ready ({2 * kv.numel() * 4 / 2**30:.2f} GiB)")
+    mx = wl.mixed_fp4(seed=5)
+    m = dict(R=mx["R"], kv=up(mx["kv"]), sc=up(mx["score"]), pos=up(mx["pos"]),
+             table=up(mx["table"]), full=up(mx["full"]),
+             loc=torch.empty(mx["cap"], dtype=torch.int32, device=dev),
+             page_ids=up(mx["page_ids"]), pool=kvq.new_pool(kvq.V41_FP4, mx["num_pages"]))
+    m["ws"] = torch.empty((mx["page_ids"].size * 64, HEAD), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log(f"mixed: R={m['R']}, pages={mx['page_ids'].size}; inputs generated in "
+        f"{time.perf_counter() - t_gen:.1f} s")
+
+    c4, c128 = inputs["c4a"], inputs["c128a"]
+    names = ["translate", "compress_mixed_fp4", "dequant_fp4", "compress_c4a", "compress_c128a"]
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        loc = kvq.kv_translate_slots(m["table"], m["full"], m["loc"])
+        if ev: ev[1].record()
+        kvq.kv_compress_store(m["pool"], kvq.V41_FP4, m["kv"], m["sc"], 4, m["pos"], cs, loc)
+        if ev: ev[2].record()
+        kvq.kv_dequant(m["pool"], kvq.V41_FP4, m["page_ids"], m["ws"])
+        if ev: ev[3].record()
+        kvq.kv_compress_store(c4["pool"], kvq.V41, c4["kv"], c4["sc"], 4, c4["pos"], cs, c4["slots"])
+        if ev: ev[4].record()
+        kvq.kv_compress_store(c128["pool"], kvq.V41, c128["kv"], c128["sc"], 128, c128["pos"], cs,
+                              c128["slots"])
+        if ev: ev[5].record()
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    per = {n: [] for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per[n].append(ev[j].elapsed_time(ev[j + 1]))
+    avg_ms = {n: float(np.mean(v)) for n, v in per.items()}
+    log("timed region done: " + ", ".join(f"{n} {avg_ms[n] * 1e3:.1f} us" for n in names))
+
+    # achievable-bandwidth reference (context): a plain 1 GiB device copy
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ce[0].record()
+    for _ in range(10):
+        dst.copy_(src)
+    ce[1].record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 4 * 10 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
+    del src, dst
+
+    pb_fp4, pb_v41 = kvq.page_bytes(kvq.V41_FP4), kvq.page_bytes(kvq.V41)
+    alg = {
+        "translate": bytes_translate(m["R"], mx["cap"]),
+        "compress_mixed_fp4": bytes_compress(m["R"], 4, kvq.bytes_per_token(kvq.V41_FP4)),
+        "dequant_fp4": bytes_dequant(mx["page_ids"].size, pb_fp4),
+        "compress_c4a": bytes_compress(16384, 4, kvq.bytes_per_token(kvq.V41)),
+        "compress_c128a": bytes_compress(16384, 128, kvq.bytes_per_token(kvq.V41)),
+    }
+    rows = {"compress_mixed_fp4": m["R"], "compress_c4a": 16384, "compress_c128a": 16384}
+    kernels = {}
+    for n in names:
+        gbs = alg[n] / (avg_ms[n] * 1e-3) / 1e9
+        kernels[n] = {"us": round(avg_ms[n] * 1e3, 2), "alg_bytes": alg[n], "GB/s": round(gbs, 1),
+                      "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        if n in rows:
+            kernels[n]["rows/s"] = round(rows[n] / (avg_ms[n] * 1e-3), 1)
+    rows_per_step = sum(rows.values())
+    dom = "compress_c128a"
+    traffic = read_traffic(alg[dom])
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        t = time.perf_counter()
+        rc, loc_h = oracle.translate_slots(mx["table"], mx["full"], mx["cap"])
+        pool = oracle.new_pool(oracle.V41_FP4, mx["num_pages"])
+        oracle.kv_compress_store(oracle.V41_FP4, pool, mx["kv"], mx["score"], 4, mx["pos"], cs_host,
+                                 loc_h[: mx["R"]].copy())
+        oracle.kv_dequant(oracle.V41_FP4, pool, mx["page_ids"])
+        t_mixed = time.perf_counter() - t
+        cpu_step = t_mixed + cpu_rows_t["c4a"] + cpu_rows_t["c128a"]
+        cpu = {"value": round(rows_per_step / cpu_step, 1), "unit": "rows/s",
+               "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": ("the whole step: every row of the mixed FP4 step, C4A and C128A, one run, "
+                          "OpenMP over rows; input generation excluded (C128A timed chunk by chunk "
+                          "as its inputs are generated)"),
+               "seconds": {"mixed_fp4": round(t_mixed, 3), "c4a": round(cpu_rows_t["c4a"], 3),
+                           "c128a": round(cpu_rows_t["c128a"], 3)}}
+        log(f"cpu oracle: {cpu['value']} rows/s on {cpu['cores']} threads ({cpu_step:.2f} s per step)")
+
+    out = {
+        "metric": METRIC,
+        "value": round(rows_per_step / (ms_per_step * 1e-3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": ("mixed V41_FP4 step (translate + ratio-4 compress + dequant) + C4A "
+                         "(R=16384, ratio 4, V41) + C128A (R=16384, ratio 128, V41); fp32 kv/score "
+                         "x 512 channels, 64-token pages"),
+            "rows_per_step": rows_per_step,
+            "mixed_rows": m["R"], "mixed_pages": int(mx["page_ids"].size),
+            "c4a_rows": 16384, "c128a_rows": 16384,
+        },
+        "roofline": {
+            "kernel": "compress_long_kernel<V41, ratio 128> (C128A)",
+            "bound": "hbm",
+            "achieved": kernels[dom]["GB/s"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": kernels[dom]["frac_of_peak"],
+            "traffic": None if traffic is None else round(traffic["bytes"]),
+        },
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "copy_1GiB_GB/s": round(copy_gbs, 1),
+        "c4a": {"rows/s": kernels["compress_c4a"]["rows/s"], "GB/s": kernels["compress_c4a"]["GB/s"],
+                "frac_of_peak": kernels["compress_c4a"]["frac_of_peak"]},
+        "c128a": {"rows/s": kernels[dom]["rows/s"], "GB/s": kernels[dom]["GB/s"],
+                  "frac_of_peak": kernels[dom]["frac_of_peak"]},
+    }
+    if traffic is not None:
+        out["roofline"]["traffic_over_algorithmic"] = round(traffic["ratio_to_algorithmic"], 4)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

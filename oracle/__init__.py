@@ -67,6 +67,7 @@ def lib():
                                    ctypes.c_uint16, ctypes.c_float, ctypes.c_double)
     vp = ctypes.c_void_p
     sig = {
+        "orc_num_threads": (ctypes.c_int, []),
         "orc_code_row_bytes": (i64, [i32]),
         "orc_scale_row_bytes": (i64, [i32]),
         "orc_bytes_per_token": (i64, [i32]),
@@ -114,6 +115,10 @@ def _ok(rc, what):
 
 
 # ------------------------------------------------------------------ scalar helpers
+def num_threads():
+    return int(lib().orc_num_threads())
+
+
 def code_row_bytes(layout):
     return int(lib().orc_code_row_bytes(layout))
 

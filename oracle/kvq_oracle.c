@@ -26,8 +26,12 @@
  * together with the test that pins it.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <string.h>
+
+/* Threads the OpenMP loops below use (reported with CPU timings). */
+int orc_num_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- layout facts */
 /* [P1] section 1: V41 keeps 512 fp8 e4m3 codes and one ue8m0 scale per 32 values

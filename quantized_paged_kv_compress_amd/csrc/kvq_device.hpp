@@ -1,12 +1,15 @@
 // kvq_device.hpp -- per-lane building blocks shared by the gfx950 kernels.
 //
-// Work mapping: one 64-lane wavefront owns one 512-channel row; lane l owns channels
-// 8l..8l+7 (one 16-byte bf16 load, or two 16-byte fp32 loads).  The eight-elements-per-
-// lane and 128-bit-load choices follow the compressor kernel of "DeepSeek V4 Sparse FP8
-// Compressor kernel optimisation with CuteDSL" (vLLM PR #44161 analysis), section 1; on a
-// 64-wide wavefront they make one wavefront cover the whole row, and a 32-value scale
-// block is exactly one 4-lane DPP quad, so the block absmax needs two DPP max steps and
-// no LDS (the wave64 counterpart of the group butterfly of that page's section 3).
+// Work mapping ("two-half" mapping): one 64-lane wavefront owns one 512-channel row and
+// lane l owns channels 4l..4l+3 (v[0..3]) and 256+4l..256+4l+3 (v[4..7]).  Every load
+// instruction of a row then covers one contiguous run (1 KiB of fp32 or 512 B of bf16)
+// -- measured on MI355X, fully contiguous 16-byte-per-lane streams reach ~7.0 TB/s where
+// a lane reading 32 contiguous bytes as two 16-byte halves tops out near 6.4 TB/s.
+// Eight values per lane and 128-bit loads follow the compressor kernel of "DeepSeek V4
+// Sparse FP8 Compressor kernel optimisation with CuteDSL" (vLLM PR #44161 analysis),
+// section 1.  A 32-value scale block is then 8 adjacent lanes (block l/8 in the first
+// half, 8 + l/8 in the second), so the block absmax is three DPP max steps with no LDS,
+// the wave64 counterpart of that page's section-3 group butterfly.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,12 +21,15 @@
 namespace kvq {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kHalf = kHeadDim / 2;                        // 256 channels per half
+constexpr int kRopeLane0 = (kHeadDim - kRopeDim - kHalf) / 4;  // 48: first lane of the rope region
+static_assert(kRopeLane0 == 48 && kRopeDim / 2 / 4 == 8, "rope pairs are lanes l and l+8 of DPP row 3");
 
 // ---------------------------------------------------------------- bf16
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// float32 -> nearest bfloat16 (ties to even), kept as a float32 value.
+// float32 -> nearest bfloat16 (ties to even): the 16-bit pattern, and the value.
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
     uint32_t u = __float_as_uint(f);
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
@@ -33,36 +39,56 @@ __device__ __forceinline__ float round_bf16(float f) {
 }
 
 // ---------------------------------------------------------------- cross-lane
-// quad_perm [1,0,3,2] and [2,3,0,1]: exchange within each group of 4 lanes.
-__device__ __forceinline__ uint32_t dpp_quad_xor1(uint32_t v) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false));
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, 0xF, 0xF, false));
 }
-__device__ __forceinline__ uint32_t dpp_quad_xor2(uint32_t v) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false));
+__device__ __forceinline__ float dppf_row_ror8(float v) {
+    return __uint_as_float(dpp<0x128>(__float_as_uint(v)));
 }
-// row_ror:4 and row_ror:8 inside each 16-lane DPP row.
-__device__ __forceinline__ uint32_t dpp_row_ror4(uint32_t v) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x124, 0xF, 0xF, false));
-}
-__device__ __forceinline__ uint32_t dpp_row_ror8(uint32_t v) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xF, 0xF, false));
+// swap lane groups of 16 inside each 32 (ds_swizzle bit mode, xor mask 0x10)
+__device__ __forceinline__ uint32_t swizzle_xor16(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x401F));
 }
 
-// Max over the 4 lanes of a quad, for non-negative float bit patterns (unsigned order
-// equals float order for them).
-__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
-    v = max(v, dpp_quad_xor1(v));
-    v = max(v, dpp_quad_xor2(v));
+// Max over each group of 8 lanes, for non-negative float bit patterns (unsigned order
+// equals float order for them): quad_perm [1,0,3,2], quad_perm [2,3,0,1], then
+// row_half_mirror, which maps each quad onto the other quad of its 8-lane half-row.
+__device__ __forceinline__ uint32_t oct_max_u32(uint32_t v) {
+    v = max(v, dpp<0xB1>(v));
+    v = max(v, dpp<0x4E>(v));
+    v = max(v, dpp<0x141>(v));
     return v;
 }
 
-// Lane l contributes one byte per quad (block l/4); returns, on every lane of a 16-lane
-// row, the dword holding the 4 bytes of that row's 4 blocks (block 4r+j in byte j).
-__device__ __forceinline__ uint32_t gather_quad_bytes(uint32_t byte, int lane) {
-    uint32_t w = byte << (8 * ((lane >> 2) & 3));
-    w |= dpp_row_ror4(w);
-    w |= dpp_row_ror8(w);
+// Lane l contributes the byte of block l/8 of one half; returns on lanes 0 and 32 the
+// dword of blocks 0..3 and 4..7 of that half (block 4r+j in byte j).
+__device__ __forceinline__ uint32_t gather_block_bytes(uint32_t byte, int lane) {
+    uint32_t w = byte << (8 * ((lane >> 3) & 3));
+    w |= dpp<0x128>(w);      // row_ror:8 joins lanes l and l^8 (blocks b, b^1)
+    w |= swizzle_xor16(w);   // joins the two DPP rows of each 32 lanes (blocks b^2)
     return w;
+}
+
+// ---------------------------------------------------------------- loads
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// This lane's 8 channels of a bf16 row (two 8-byte loads; each instruction reads 512
+// contiguous bytes across the wavefront).
+__device__ __forceinline__ void load_row_bf16(const uint16_t* __restrict__ row, int lane, float (&v)[8]) {
+    const uint2 a = *reinterpret_cast<const uint2*>(row + 4 * lane);
+    const uint2 b = *reinterpret_cast<const uint2*>(row + kHalf + 4 * lane);
+    v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+    v[4] = bf16_lo(b.x); v[5] = bf16_hi(b.x); v[6] = bf16_lo(b.y); v[7] = bf16_hi(b.y);
+}
+
+// This lane's 8 channels of an fp32 row: two non-temporal 16-byte loads (each
+// instruction reads 1 KiB contiguous); streaming inputs are read exactly once.
+__device__ __forceinline__ void load_row_f32(const float* __restrict__ row, int lane, float (&v)[8]) {
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 4 * lane));
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + kHalf + 4 * lane));
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
 // ---------------------------------------------------------------- e4m3 / e2m1
@@ -85,101 +111,121 @@ __device__ __forceinline__ float e4m3_mag_value(uint32_t c) {
 }
 
 // ---------------------------------------------------------------- RoPE
-// NeoX half rotation of channels 448..511 (lanes 56..63): channel 448+i (lane 56 + i/8)
-// pairs with 480+i (lane 60 + i/8), i.e. lanes l and l^4.  cos_sin_row holds the 32
-// cosines then the 32 sines of the position.  Products and sums are rounded one at a
-// time (the file is compiled without contraction) and the results rounded to bf16.
-// Every lane must call this (the partner exchange is wave-wide).
-__device__ __forceinline__ void rope_lane(float (&v)[8], const float* __restrict__ cos_sin_row,
-                                          int lane) {
-    float p[8];
+// NeoX half rotation of channels 448..511: channel 448+i is the second-half value
+// v[4 + i%4] of lane 48 + i/4 and its partner 480+i sits in lane 56 + i/4, i.e. lanes
+// l and l+8 of DPP row 3, exchanged with one row_ror:8 per value.  The cosines and sines
+// of a lane's four angles (i = 4*(l%8) .. +3) are loaded ahead by rope_load_cs.
+struct RopeCS {
+    float c[4], s[4];
+};
+
+__device__ __forceinline__ void rope_load_cs(const float* __restrict__ cos_sin_row, int lane, RopeCS& cs) {
+    if (lane >= kRopeLane0) {
+        const int i0 = 4 * (lane & 7);
+        const float4 c = *reinterpret_cast<const float4*>(cos_sin_row + i0);
+        const float4 s = *reinterpret_cast<const float4*>(cos_sin_row + kRopeDim / 2 + i0);
+        cs.c[0] = c.x; cs.c[1] = c.y; cs.c[2] = c.z; cs.c[3] = c.w;
+        cs.s[0] = s.x; cs.s[1] = s.y; cs.s[2] = s.z; cs.s[3] = s.w;
+    }
+}
+
+// Products and sums are rounded one at a time (the file is compiled without
+// contraction) and the results rounded to bf16.  Every lane must call this.
+__device__ __forceinline__ void rope_apply(float (&v)[8], const RopeCS& cs, int lane) {
+    float p[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = __shfl_xor(v[e], 4);
-    if (lane >= kWave - kRopeDim / kElemsPerLane) {
-        const int i0 = (lane & 3) * kElemsPerLane;
-        const float4 c0 = *reinterpret_cast<const float4*>(cos_sin_row + i0);
-        const float4 c1 = *reinterpret_cast<const float4*>(cos_sin_row + i0 + 4);
-        const float4 s0 = *reinterpret_cast<const float4*>(cos_sin_row + kRopeDim / 2 + i0);
-        const float4 s1 = *reinterpret_cast<const float4*>(cos_sin_row + kRopeDim / 2 + i0 + 4);
-        const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-        const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-        const bool first_half = lane < kWave - kRopeDim / (2 * kElemsPerLane);
+    for (int e = 0; e < 4; ++e) p[e] = dppf_row_ror8(v[4 + e]);
+    if (lane >= kRopeLane0) {
+        const bool first = lane < kRopeLane0 + 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float a = v[e] * c[e];
-            const float b = p[e] * s[e];
-            v[e] = round_bf16(first_half ? a - b : a + b);
+        for (int e = 0; e < 4; ++e) {
+            const float a = v[4 + e] * cs.c[e];
+            const float b = p[e] * cs.s[e];
+            v[4 + e] = round_bf16(first ? a - b : a + b);
         }
     }
 }
 
 // ---------------------------------------------------------------- quantise + store
 // Quantise this lane's 8 bf16-valued floats of a row and write its share of the row at
-// `slot` (the caller has checked the slot is inside the pool).
+// `slot` (the caller has checked the slot is inside the pool).  Every lane must call
+// this.
 template <Layout L>
 __device__ __forceinline__ void quantize_store_row(uint8_t* __restrict__ pool, uint32_t slot,
                                                    const float (&v)[8], int lane) {
     using PK = PagedKV<L, kPageBits>;
-    uint32_t amax_bits = 0;
+    uint32_t amax[2] = {0, 0};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax_bits = max(amax_bits, __float_as_uint(v[e]) & 0x7FFFFFFFu);
-    amax_bits = quad_max_u32(amax_bits);
+    for (int e = 0; e < 8; ++e) amax[e >> 2] = max(amax[e >> 2], __float_as_uint(v[e]) & 0x7FFFFFFFu);
+    amax[0] = oct_max_u32(amax[0]);
+    amax[1] = oct_max_u32(amax[1]);
 
     uint8_t* code_row = PK::code_row(pool, slot);
     uint8_t* scale_row = PK::scale_row(pool, slot);
-    uint32_t scale_byte;
+    uint32_t sbyte[2];
 
     if constexpr (L == Layout::V41) {
         // ue8m0: smallest k >= -127 with amax <= 448 * 2^k.  With amax = 2^E * (1+f),
         // amax / 448 = 2^(E-8) * (1+f) / 1.75, so k = E - 8 + (1+f > 1.75): read off the
         // exponent and mantissa bits, no division.  Byte = k + 127, clamped at 0.
-        const int biased = static_cast<int>(amax_bits >> 23);
-        const int byte = max(0, biased - 8 + static_cast<int>((amax_bits & 0x7FFFFFu) > 0x600000u));
-        scale_byte = static_cast<uint32_t>(byte);
-        const float inv_scale = __uint_as_float(static_cast<uint32_t>(254 - byte) << 23);  // 2^-k
-        uint32_t lo = 0, hi = 0;
+        uint32_t word[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t sign = (__float_as_uint(v[e]) >> 24) & 0x80u;
-            const uint32_t code = e4m3_mag_code(fabsf(v[e]) * inv_scale) | sign;  // exact scaling
-            if (e < 4) lo |= code << (8 * e);
-            else hi |= code << (8 * (e - 4));
+        for (int h = 0; h < 2; ++h) {
+            const int biased = static_cast<int>(amax[h] >> 23);
+            const int byte = max(0, biased - 8 + static_cast<int>((amax[h] & 0x7FFFFFu) > 0x600000u));
+            sbyte[h] = static_cast<uint32_t>(byte);
+            const float inv_scale = __uint_as_float(static_cast<uint32_t>(254 - byte) << 23);  // 2^-k
+            // x * 2^-k is exact; the gfx950 pack convert rounds to nearest even into OCP
+            // e4m3fn with the sign kept (|x * 2^-k| <= 448, so it never saturates).
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * h] * inv_scale, v[4 * h + 1] * inv_scale, 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * h + 2] * inv_scale, v[4 * h + 3] * inv_scale, w, true);
+            word[h] = static_cast<uint32_t>(w);
         }
-        *reinterpret_cast<uint2*>(code_row + kElemsPerLane * lane) = make_uint2(lo, hi);
+        *reinterpret_cast<uint32_t*>(code_row + 4 * lane) = word[0];
+        *reinterpret_cast<uint32_t*>(code_row + kHalf + 4 * lane) = word[1];
     } else {
         // e4m3 scale = RNE(fl32(amax / 6)), held at 448; codes = e2m1 RNE of fl32(x / s).
         // fl32(x / s) lands exactly on a rounding midpoint t only when x / s == t (x has 8
         // significant bits, s 4, t 3), so the code equals counting the midpoints t*s
         // (exact products) that |x| passes, with ">=" at midpoints whose upper
         // neighbour has the even code.
-        const float amax = __uint_as_float(amax_bits);
-        const float t = amax / 6.0f;  // IEEE-correct single-precision division
-        const uint32_t sc = min(e4m3_mag_code(t), 0x7Eu);
-        scale_byte = sc;
-        const float s = e4m3_mag_value(sc);
-        const float m0 = 0.25f * s, m1 = 0.75f * s, m2 = 1.25f * s, m3 = 1.75f * s;
-        const float m4 = 2.5f * s, m5 = 3.5f * s, m6 = 5.0f * s;
-        uint32_t word = 0;
+        uint32_t half_word[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float a = fabsf(v[e]);
-            uint32_t c = static_cast<uint32_t>(a > m0) + static_cast<uint32_t>(a >= m1) +
-                         static_cast<uint32_t>(a > m2) + static_cast<uint32_t>(a >= m3) +
-                         static_cast<uint32_t>(a > m4) + static_cast<uint32_t>(a >= m5) +
-                         static_cast<uint32_t>(a > m6);
-            c |= (__float_as_uint(v[e]) >> 28) & 8u;
-            word |= c << (4 * e);
+        for (int h = 0; h < 2; ++h) {
+            const float t = __uint_as_float(amax[h]) / 6.0f;  // IEEE-correct division
+            const uint32_t sc = min(e4m3_mag_code(t), 0x7Eu);
+            sbyte[h] = sc;
+            const float s = e4m3_mag_value(sc);
+            const float m0 = 0.25f * s, m1 = 0.75f * s, m2 = 1.25f * s, m3 = 1.75f * s;
+            const float m4 = 2.5f * s, m5 = 3.5f * s, m6 = 5.0f * s;
+            uint32_t w = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x = v[4 * h + e];
+                const float a = fabsf(x);
+                uint32_t c = static_cast<uint32_t>(a > m0) + static_cast<uint32_t>(a >= m1) +
+                             static_cast<uint32_t>(a > m2) + static_cast<uint32_t>(a >= m3) +
+                             static_cast<uint32_t>(a > m4) + static_cast<uint32_t>(a >= m5) +
+                             static_cast<uint32_t>(a > m6);
+                c |= (__float_as_uint(x) >> 28) & 8u;
+                w |= c << (4 * e);
+            }
+            half_word[h] = sc == 0 ? 0u : w;  // a zero scale stores all-zero codes
         }
-        if (sc == 0) word = 0;  // a zero scale stores all-zero codes
-        *reinterpret_cast<uint32_t*>(code_row + LayoutTraits<L>::kCodeBytesPerLane * lane) = word;
+        *reinterpret_cast<uint16_t*>(code_row + 2 * lane) = static_cast<uint16_t>(half_word[0]);
+        *reinterpret_cast<uint16_t*>(code_row + kHalf / 2 + 2 * lane) = static_cast<uint16_t>(half_word[1]);
     }
 
-    // Scale row: lane 16r writes the dword of blocks 4r..4r+3; FP4 lanes 16r+1 zero the
-    // pad dword r.  Four (eight) lanes of one store instruction cover the 16 (32) bytes.
-    const uint32_t sw = gather_quad_bytes(scale_byte, lane);
-    if ((lane & 15) == 0) *reinterpret_cast<uint32_t*>(scale_row + 4 * (lane >> 4)) = sw;
-    if constexpr (L == Layout::V41_FP4) {
-        if ((lane & 15) == 1) *reinterpret_cast<uint32_t*>(scale_row + kBlocks + 4 * (lane >> 4)) = 0u;
+    // Scale row: lanes 0 and 32 hold the dwords of blocks 0-3 / 4-7 (first half) and
+    // 8-11 / 12-15 (second half).  FP4 rows also get their 16 zero pad bytes.
+    const uint32_t w0 = gather_block_bytes(sbyte[0], lane);
+    const uint32_t w1 = gather_block_bytes(sbyte[1], lane);
+    if ((lane & 31) == 0) {
+        const int q = lane >> 5;
+        *reinterpret_cast<uint32_t*>(scale_row + 4 * q) = w0;
+        *reinterpret_cast<uint32_t*>(scale_row + 8 + 4 * q) = w1;
+        if constexpr (L == Layout::V41_FP4)
+            *reinterpret_cast<uint2*>(scale_row + kBlocks + 8 * q) = make_uint2(0u, 0u);
     }
 }
 

@@ -20,26 +20,8 @@ __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
 }
 
-__device__ __forceinline__ void load_bf16x8(const uint16_t* __restrict__ p, float (&v)[8]) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p);
-    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
-    v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
-    v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
-}
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// Streaming fp32 inputs are read once: non-temporal 16-byte loads.
-__device__ __forceinline__ void load_f32x8(const float* __restrict__ p, float (&v)[8]) {
-    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
 // ------------------------------------------------------------------ store / store+RoPE
-// One wavefront per bf16 row: load 16 B per lane, optional RoPE, quantise, store.
+// One wavefront per bf16 row: two 8-byte loads per lane, optional RoPE, quantise, store.
 template <Layout L, bool kRope>
 __global__ __launch_bounds__(kWave * kRowsPerBlock) void store_kernel(
     uint8_t* __restrict__ pool, int64_t nslots, const uint16_t* __restrict__ k, int64_t ld,
@@ -50,21 +32,24 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void store_kernel(
     if (i >= n) return;
     const int32_t slot = slots[i];
     if (slot < 0 || slot >= nslots) return;
-    int32_t p = 0;
+    RopeCS cs;
     if constexpr (kRope) {
-        p = pos[i];
+        const int32_t p = pos[i];
         if (p < 0 || p >= max_pos) return;
+        rope_load_cs(cos_sin + static_cast<int64_t>(p) * kRopeDim, lane, cs);
     }
     float v[8];
-    load_bf16x8(k + i * ld + kElemsPerLane * lane, v);
-    if constexpr (kRope) rope_lane(v, cos_sin + static_cast<int64_t>(p) * kRopeDim, lane);
+    load_row_bf16(k + i * ld, lane, v);
+    if constexpr (kRope) rope_apply(v, cs, lane);
     quantize_store_row<L>(pool, static_cast<uint32_t>(slot), v, lane);
 }
 
 // ------------------------------------------------------------------ short-window compressor
 // Ratio r <= 4: one wavefront per output row; the r window rows of kv and score are all
-// loaded up front (2r + 2r 16-byte loads per lane in flight), so the per-channel maximum
-// is exact and needs no online rescaling.  Ratio 1 is the identity and skips the scores.
+// loaded up front (4r 16-byte loads per lane in flight), so the per-channel maximum is
+// exact and needs no online rescaling.  The loads and the cos/sin gather are issued
+// before the slot / position checks (which only gate the stores), so a wavefront waits
+// on memory once.  Ratio 1 is the identity and skips the scores.
 template <Layout L, int kRatio>
 __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_short_kernel(
     uint8_t* __restrict__ pool, int64_t nslots, const float* __restrict__ kv,
@@ -73,23 +58,28 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_short_kernel(
     int64_t R) {
     static_assert(kRatio >= 1 && kRatio <= 4, "short window");
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave_id();
-    if (i >= R) return;
+    const int64_t i_raw = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave_id();
+    const int64_t i = i_raw < R ? i_raw : R - 1;  // rows past R (last block) read row R-1, store nothing
+
+    const int64_t base = i * kRatio * ld;
+    float x[kRatio][8];
+    float s[kRatio > 1 ? kRatio : 1][8];
+#pragma unroll
+    for (int j = 0; j < kRatio; ++j) {
+        load_row_f32(kv + base + j * ld, lane, x[j]);
+        if constexpr (kRatio > 1) load_row_f32(score + base + j * ld, lane, s[j]);
+    }
     const int32_t slot = slots[i];
     const int32_t p = pos[i];
-    if (slot < 0 || slot >= nslots || p < 0 || p >= max_pos) return;
+    const bool valid = i_raw < R && slot >= 0 && slot < nslots && p >= 0 && p < max_pos;
+    RopeCS cs;
+    rope_load_cs(cos_sin + static_cast<int64_t>(valid ? p : 0) * kRopeDim, lane, cs);
 
-    const int64_t base = i * kRatio * ld + kElemsPerLane * lane;
     float v[8];
     if constexpr (kRatio == 1) {
-        load_f32x8(kv + base, v);
-    } else {
-        float x[kRatio][8], s[kRatio][8];
 #pragma unroll
-        for (int j = 0; j < kRatio; ++j) {
-            load_f32x8(kv + base + j * ld, x[j]);
-            load_f32x8(score + base + j * ld, s[j]);
-        }
+        for (int e = 0; e < 8; ++e) v[e] = x[0][e];
+    } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float m = s[0][e];
@@ -108,17 +98,52 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_short_kernel(
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = round_bf16(v[e]);
-    rope_lane(v, cos_sin + static_cast<int64_t>(p) * kRopeDim, lane);
+    rope_apply(v, cs, lane);
+    if (!valid) return;
     quantize_store_row<L>(pool, static_cast<uint32_t>(slot), v, lane);
 }
 
 // ------------------------------------------------------------------ long-window compressor
 // Large ratios (128): one workgroup of kWaves wavefronts per output row.  Wavefront w
-// streams window rows [w*r/kWaves, (w+1)*r/kWaves) in chunks of kChunk rows, keeping a
-// per-channel online softmax state (running max m, denominator l, numerator acc) in
-// registers (the online form of the vLLM page's section 2, rescaling once per chunk).
-// The kWaves partial states are merged through LDS by wavefront 0 -- the only LDS use in
-// the library -- which then rounds, rotates, quantises and stores the row.
+// streams window rows [w*r/kWaves, (w+1)*r/kWaves) in chunks of kChunk rows, double
+// buffered (the next chunk's loads are in flight while the current chunk is folded in),
+// keeping a per-channel online softmax state -- running max m (log2 units), denominator
+// l, numerator acc -- in registers; it rescales once per chunk (the online form of the
+// vLLM page's section 2).  The kWaves partial states are merged through LDS by
+// wavefront 0 -- the only LDS use in the library -- which then rounds, rotates,
+// quantises and stores the row.
+template <int kChunk>
+__device__ __forceinline__ void load_chunk(const float* __restrict__ kv, const float* __restrict__ score,
+                                           int64_t base, int64_t ld, int lane, float (&x)[kChunk][8],
+                                           float (&s)[kChunk][8]) {
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+        load_row_f32(kv + base + j * ld, lane, x[j]);
+        load_row_f32(score + base + j * ld, lane, s[j]);
+    }
+}
+
+template <int kChunk>
+__device__ __forceinline__ void fold_chunk(const float (&x)[kChunk][8], const float (&s)[kChunk][8],
+                                           float (&m)[8], float (&l)[8], float (&acc)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float cm = s[0][e];
+#pragma unroll
+        for (int j = 1; j < kChunk; ++j) cm = fmaxf(cm, s[j][e]);
+        const float mn = fmaxf(m[e], cm * kLog2e);
+        const float alpha = __builtin_amdgcn_exp2f(m[e] - mn);
+        float le = l[e] * alpha, ae = acc[e] * alpha;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            const float wt = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][e], kLog2e, -mn));
+            le += wt;
+            ae = __builtin_fmaf(wt, x[j][e], ae);
+        }
+        m[e] = mn; l[e] = le; acc[e] = ae;
+    }
+}
+
 template <Layout L, int kRatio, int kWaves, int kChunk>
 __global__ __launch_bounds__(kWave * kWaves) void compress_long_kernel(
     uint8_t* __restrict__ pool, int64_t nslots, const float* __restrict__ kv,
@@ -126,7 +151,7 @@ __global__ __launch_bounds__(kWave * kWaves) void compress_long_kernel(
     const float* __restrict__ cos_sin, int64_t max_pos, const int32_t* __restrict__ slots,
     int64_t R) {
     constexpr int kRowsPerWave = kRatio / kWaves;
-    static_assert(kRatio % kWaves == 0 && kRowsPerWave % kChunk == 0, "window split");
+    static_assert(kRatio % kWaves == 0 && kRowsPerWave % (2 * kChunk) == 0, "window split");
     __shared__ float4 part[kWaves - 1][3][kWave * 2];
 
     const int64_t i = blockIdx.x;
@@ -136,38 +161,25 @@ __global__ __launch_bounds__(kWave * kWaves) void compress_long_kernel(
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = wave_id();
-    const int64_t base = (i * kRatio + static_cast<int64_t>(w) * kRowsPerWave) * ld + kElemsPerLane * lane;
+    const int64_t base = (i * kRatio + static_cast<int64_t>(w) * kRowsPerWave) * ld;
 
-    float m[8], l[8], acc[8];  // m in log2 units
+    float m[8], l[8], acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) { m[e] = -__builtin_inff(); l[e] = 0.0f; acc[e] = 0.0f; }
 
+    float xa[kChunk][8], sa[kChunk][8], xb[kChunk][8], sb[kChunk][8];
+    load_chunk<kChunk>(kv, score, base, ld, lane, xa, sa);
 #pragma unroll 1
-    for (int c = 0; c < kRowsPerWave; c += kChunk) {
-        float x[kChunk][8], s[kChunk][8];
-#pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-            load_f32x8(kv + base + (c + j) * ld, x[j]);
-            load_f32x8(score + base + (c + j) * ld, s[j]);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float cm = s[0][e];
-#pragma unroll
-            for (int j = 1; j < kChunk; ++j) cm = fmaxf(cm, s[j][e]);
-            const float mn = fmaxf(m[e], cm * kLog2e);
-            const float alpha = __builtin_amdgcn_exp2f(m[e] - mn);
-            float le = l[e] * alpha, ae = acc[e] * alpha;
-#pragma unroll
-            for (int j = 0; j < kChunk; ++j) {
-                const float wt = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][e], kLog2e, -mn));
-                le += wt;
-                ae = __builtin_fmaf(wt, x[j][e], ae);
-            }
-            m[e] = mn; l[e] = le; acc[e] = ae;
-        }
+    for (int c = 0; c < kRowsPerWave; c += 2 * kChunk) {
+        load_chunk<kChunk>(kv, score, base + (c + kChunk) * ld, ld, lane, xb, sb);
+        fold_chunk<kChunk>(xa, sa, m, l, acc);
+        if (c + 2 * kChunk < kRowsPerWave)
+            load_chunk<kChunk>(kv, score, base + (c + 2 * kChunk) * ld, ld, lane, xa, sa);
+        fold_chunk<kChunk>(xb, sb, m, l, acc);
     }
 
+    RopeCS cs;
+    if (w == 0) rope_load_cs(cos_sin + static_cast<int64_t>(p) * kRopeDim, lane, cs);
     if (w != 0) {
         float4* dst = &part[w - 1][0][2 * lane];
         dst[0] = make_float4(m[0], m[1], m[2], m[3]);
@@ -182,36 +194,29 @@ __global__ __launch_bounds__(kWave * kWaves) void compress_long_kernel(
     __syncthreads();
     if (w != 0) return;
 
-    float pm[kWaves - 1][8], pl[kWaves - 1][8], pa[kWaves - 1][8];
-#pragma unroll
-    for (int q = 0; q < kWaves - 1; ++q) {
-        const float4* src = &part[q][0][2 * lane];
-        pm[q][0] = src[0].x; pm[q][1] = src[0].y; pm[q][2] = src[0].z; pm[q][3] = src[0].w;
-        pm[q][4] = src[1].x; pm[q][5] = src[1].y; pm[q][6] = src[1].z; pm[q][7] = src[1].w;
-        src = &part[q][1][2 * lane];
-        pl[q][0] = src[0].x; pl[q][1] = src[0].y; pl[q][2] = src[0].z; pl[q][3] = src[0].w;
-        pl[q][4] = src[1].x; pl[q][5] = src[1].y; pl[q][6] = src[1].z; pl[q][7] = src[1].w;
-        src = &part[q][2][2 * lane];
-        pa[q][0] = src[0].x; pa[q][1] = src[0].y; pa[q][2] = src[0].z; pa[q][3] = src[0].w;
-        pa[q][4] = src[1].x; pa[q][5] = src[1].y; pa[q][6] = src[1].z; pa[q][7] = src[1].w;
-    }
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
+        float pm[kWaves - 1], pl[kWaves - 1], pa[kWaves - 1];
         float M = m[e];
 #pragma unroll
-        for (int q = 0; q < kWaves - 1; ++q) M = fmaxf(M, pm[q][e]);
+        for (int q = 0; q < kWaves - 1; ++q) {
+            pm[q] = reinterpret_cast<const float*>(&part[q][0][2 * lane])[e];
+            pl[q] = reinterpret_cast<const float*>(&part[q][1][2 * lane])[e];
+            pa[q] = reinterpret_cast<const float*>(&part[q][2][2 * lane])[e];
+            M = fmaxf(M, pm[q]);
+        }
         const float a0 = __builtin_amdgcn_exp2f(m[e] - M);
         float den = l[e] * a0, num = acc[e] * a0;
 #pragma unroll
         for (int q = 0; q < kWaves - 1; ++q) {
-            const float a = __builtin_amdgcn_exp2f(pm[q][e] - M);
-            den = __builtin_fmaf(pl[q][e], a, den);
-            num = __builtin_fmaf(pa[q][e], a, num);
+            const float a = __builtin_amdgcn_exp2f(pm[q] - M);
+            den = __builtin_fmaf(pl[q], a, den);
+            num = __builtin_fmaf(pa[q], a, num);
         }
         v[e] = round_bf16(num * __builtin_amdgcn_rcpf(den));
     }
-    rope_lane(v, cos_sin + static_cast<int64_t>(p) * kRopeDim, lane);
+    rope_apply(v, cs, lane);
     quantize_store_row<L>(pool, static_cast<uint32_t>(slot), v, lane);
 }
 
