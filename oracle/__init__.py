@@ -62,7 +62,26 @@ def lib():
         return _lib
     if not os.path.exists(_build.LIB):
         _build.build()
-    L = ctypes.CDLL(_build.LIB)
+    _lib = _load(_build.LIB)
+    return _lib
+
+
+def use_library(path):
+    """Swap in another build of the oracle (the mutation tests plant mistakes in copies
+    of kvq_oracle.c); returns the previous handle, which use_handle() restores."""
+    global _lib
+    prev = _lib
+    _lib = _load(path)
+    return prev
+
+
+def use_handle(handle):
+    global _lib
+    _lib = handle
+
+
+def _load(path):
+    L = ctypes.CDLL(path)
     i32, i64, u8, u16, f32, f64 = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint8,
                                    ctypes.c_uint16, ctypes.c_float, ctypes.c_double)
     vp = ctypes.c_void_p
@@ -95,7 +114,6 @@ def lib():
         fn = getattr(L, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = L
     return L
 
 

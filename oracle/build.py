@@ -12,12 +12,13 @@ SRC = os.path.join(HERE, "kvq_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
+def command(src=SRC, out=LIB):
+    return ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+            "-fno-fast-math", "-Wall", "-Wextra", src, "-o", out, "-lm"]
+
+
 def build(verbose: bool = False) -> str:
-    cmd = [
-        "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
-        "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
-        SRC, "-o", LIB + ".tmp", "-lm",
-    ]
+    cmd = command(SRC, LIB + ".tmp")
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

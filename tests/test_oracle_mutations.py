@@ -1,0 +1,112 @@
+"""Planted mistakes: each plausible slip in the oracle must fail at least one pin.
+
+Every case copies oracle/kvq_oracle.c, changes one expression, builds the copy with the
+oracle's own gcc command into a temporary directory, swaps it in, and runs the pins that
+cover that part.  The test passes only if some pin rejects the mutant; the real oracle is
+restored afterwards.  Nothing here touches the GPU.
+"""
+import json
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from oracle import build as oracle_build
+import test_oracle_pins as pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def golden(name):
+    with open(os.path.join(ROOT, "tests", "golden", name)) as f:
+        return json.load(f)
+
+
+# (name, original text, mutated text, pins that must catch it)
+MUTATIONS = [
+    ("rope sign flipped", "float o1 = a - b, o2 = d + e;", "float o1 = a + b, o2 = d - e;",
+     ["rope_pairs"]),
+    ("cos and sin swapped", "float c = cs[i], s = cs[half + i];", "float c = cs[half + i], s = cs[i];",
+     ["rope_pos0", "rope_pairs"]),
+    ("ue8m0 one power too high", "(double)amax > ldexp(448.0, k)) k++;",
+     "(double)amax > ldexp(448.0, k + 1)) k++;", ["ue8m0", "v41_worked"]),
+    ("e4m3 ties rounded up", "double n = nearbyint(a / quantum);", "double n = floor(a / quantum + 0.5);",
+     ["e4m3_exhaustive", "v41_worked"]),
+    ("e2m1 ties to odd", "(d == bestd && (i % 2) == 0)", "(d == bestd && (i % 2) == 1)",
+     ["fp4_worked", "fp4_pairs"]),
+    ("fp4 scale amax/4", "float t = amax / 6.0f;", "float t = amax / 4.0f;",
+     ["fp4_scale", "fp4_worked"]),
+    ("nibbles swapped", "(uint8_t)(lo | (hi << 4))", "(uint8_t)(hi | (lo << 4))",
+     ["fp4_worked", "byte_order"]),
+    ("window rows transposed", "(i * ratio + j) * ld", "(i + j * ratio) * ld",
+     ["pool_tiny", "pool_window"]),
+    ("softmax not normalised", "out[c] = num / den;", "out[c] = num;",
+     ["pool_tiny", "pool_mean"]),
+    ("scale rows reversed in the page", "*scale = pg + kPageRows * cr + row * sr;",
+     "*scale = pg + kPageRows * cr + (kPageRows - 1 - row) * sr;", ["addressing"]),
+    ("bf16 truncates", "double r = nearbyint(m);", "double r = trunc(m);",
+     ["bf16_torch", "bf16_brute"]),
+    ("dequant exponent shifted", "s = ldexp(1.0, (int)scale - 127);", "s = ldexp(1.0, (int)scale - 128);",
+     ["dequant_worked", "dequant_v41"]),
+    ("translate tail not zeroed", "for (int64_t i = n; i < cap; i++) out[i] = 0;",
+     "for (int64_t i = n; i < cap; i++) out[i] = -1;", ["translate"]),
+    ("fp4 padding not written", "memset(scale + kHead / kBlock, 0, 16); /* documented padding */",
+     "(void)0; /* padding left as it was */", ["addressing"]),
+]
+
+PINS = {
+    "rope_pairs": lambda o: pins.test_rope_pairs_and_rotation_direction(o),
+    "rope_pos0": lambda o: pins.test_rope_position_zero_is_identity(o),
+    "ue8m0": lambda o: pins.test_ue8m0_exhaustive_bf16_amax(o),
+    "v41_worked": lambda o: pins.test_v41_worked_examples(o, golden),
+    "e4m3_exhaustive": lambda o: pins.test_e4m3_encode_exhaustive_bf16_inputs(o),
+    "fp4_worked": lambda o: pins.test_fp4_worked_examples(o, golden),
+    "fp4_pairs": lambda o: pins.test_fp4_codes_exhaustive_pairs(o),
+    "fp4_scale": lambda o: pins.test_fp4_scale_exhaustive_bf16_amax(o),
+    "byte_order": lambda o: pins.test_store_layout_byte_and_nibble_order(o),
+    "pool_tiny": lambda o: pins.test_pool_brute_force_tiny(o, 4, 3),
+    "pool_window": lambda o: pins.test_pool_window_indexing(o),
+    "pool_mean": lambda o: pins.test_pool_equal_scores_give_mean_and_dominant_row_wins(o),
+    "addressing": lambda o: (pins.test_addressing_brute_force_with_canaries(o, 1),
+                             pins.test_addressing_brute_force_with_canaries(o, 2)),
+    "bf16_torch": lambda o: pins.test_bf16_rounding_matches_torch_on_float32(o),
+    "bf16_brute": lambda o: pins.test_bf16_rounding_from_double_brute_force(o),
+    "dequant_worked": lambda o: pins.test_dequant_worked_examples(o, golden),
+    "dequant_v41": lambda o: pins.test_dequant_exhaustive_v41(o),
+    "translate": lambda o: pins.test_translate_semantics(o, golden),
+}
+
+
+def test_every_pin_name_exists():
+    for _, _, _, names in MUTATIONS:
+        for n in names:
+            assert n in PINS
+
+
+@pytest.mark.parametrize("name,old,new,pin_names", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new, pin_names):
+    src = open(oracle_build.SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old}"
+    mutant = tmp_path / "kvq_oracle_mutant.c"
+    mutant.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mutant.so"
+    subprocess.run(oracle_build.command(str(mutant), str(lib)), check=True,
+                   stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+    prev = oracle.use_library(str(lib))
+    caught = []
+    try:
+        for pn in pin_names:
+            try:
+                PINS[pn](oracle)
+            except (AssertionError, ValueError) as e:
+                caught.append((pn, type(e).__name__))
+    finally:
+        oracle.use_handle(prev)
+    assert caught, f"no pin caught the planted mistake '{name}'"
+
+
+def test_real_oracle_passes_the_same_pins():
+    oracle.lib()
+    for fn in PINS.values():
+        fn(oracle)
