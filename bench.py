@@ -82,12 +82,99 @@ def read_traffic(duration_key_bytes):
         return None
 
 
+def micro_bench(kvq, wl, dev, cs, layers=61, reps=20, calls=50):
+    """Graph-replayed per-launch latency of the kernels in P1's latency table (store,
+    store+RoPE, c1, c2 at 1/8/64/512 tokens, V41, hot inputs), and the P2 hoisting case:
+    one full->SWA translation reused by `layers` per-layer store+RoPE calls, against a
+    translation inside every layer."""
+    import numpy as np
+    import torch
+
+    def graph_us(fn, n_calls):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n_calls):
+                fn()
+        for _ in range(3):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(reps):
+            e0.record()
+            g.replay()
+            e1.record()
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / n_calls)
+        return float(np.median(times))
+
+    def t(a):
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    rng = np.random.default_rng(123)
+    num_pages = 4096
+    pool = kvq.new_pool(kvq.V41, num_pages)
+    table = {}
+    for bs in (1, 8, 64, 512):
+        k = t(wl.bf16_bits(rng.standard_normal((bs, HEAD)).astype(np.float32)))
+        pos = t(rng.integers(0, 65536, bs).astype(np.int32))
+        slots = t(wl.distinct_slots(rng, bs, 64, num_pages * 64))
+        kv = t(rng.standard_normal((2 * bs, HEAD)).astype(np.float32))
+        sc = t((2 * rng.standard_normal((2 * bs, HEAD))).astype(np.float32))
+        fns = {
+            "store": lambda: kvq.kv_store(pool, kvq.V41, k, slots),
+            "store_rope": lambda: kvq.kv_store_rope(pool, kvq.V41, k, pos, cs, slots),
+            "c1": lambda: kvq.kv_compress_store(pool, kvq.V41, kv[:bs], None, 1, pos, cs, slots),
+            "c2": lambda: kvq.kv_compress_store(pool, kvq.V41, kv, sc, 2, pos, cs, slots),
+        }
+        for name, fn in fns.items():
+            table.setdefault(name, {})[f"bs{bs}"] = round(graph_us(fn, calls), 3)
+
+    # P2: translate once per step vs once per layer, 512 new tokens, `layers` layers
+    n, cap = 512, 4096
+    swa_pages = 64
+    full = t((rng.permutation(swa_pages * 64)[:n] + 64 * 8).astype(np.int32))
+    tab = np.full(64 * 8 + swa_pages * 64, -1, np.int32)
+    tab[64 * 8:64 * 8 + swa_pages * 64] = rng.permutation(swa_pages * 64).astype(np.int32)
+    tab = t(tab)
+    buf = torch.empty(cap, dtype=torch.int32, device=dev)
+    k = t(wl.bf16_bits(rng.standard_normal((n, HEAD)).astype(np.float32)))
+    pos = t(rng.integers(0, 65536, n).astype(np.int32))
+    pools = [kvq.new_pool(kvq.V41, swa_pages) for _ in range(layers)]
+
+    def hoisted():
+        loc = kvq.kv_translate_slots(tab, full, buf)
+        for p in pools:
+            kvq.kv_store_rope(p, kvq.V41, k, pos, cs, loc)
+
+    def per_layer():
+        for p in pools:
+            loc = kvq.kv_translate_slots(tab, full, buf)
+            kvq.kv_store_rope(p, kvq.V41, k, pos, cs, loc)
+
+    step = {"layers": layers, "tokens": n,
+            "hoisted_us_per_step": round(graph_us(hoisted, 1), 2),
+            "per_layer_translate_us_per_step": round(graph_us(per_layer, 1), 2)}
+    return {"method": f"HIP graph of {calls} back-to-back launches, median of {reps} replays, "
+                      "per-launch microseconds, V41, hot inputs",
+            "latency_us": table, "swa_hoisting": step}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-micro", action="store_true",
+                    help="skip the graph-replayed latency table and the hoisting case")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -227,6 +314,11 @@ def main():
     dom = "compress_c128a"
     traffic = read_traffic(alg[dom])
 
+    micro = None
+    if not args.no_micro:
+        micro = micro_bench(kvq, wl, dev, cs)
+        log(f"micro: {micro['latency_us']}; hoisting {micro['swa_hoisting']}")
+
     # ------------------------------------------------------------ CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -280,6 +372,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "copy_1GiB_GB/s": round(copy_gbs, 1),
+        "micro": micro,
         "c4a": {"rows/s": kernels["compress_c4a"]["rows/s"], "GB/s": kernels["compress_c4a"]["GB/s"],
                 "frac_of_peak": kernels["compress_c4a"]["frac_of_peak"]},
         "c128a": {"rows/s": kernels[dom]["rows/s"], "GB/s": kernels[dom]["GB/s"],
