@@ -66,7 +66,7 @@ extern "C" {
 #define KVQ_EINVAL (-1)    /* null pointer with work to do, ld < 512, misaligned
                               pointer or stride, negative size, max_pos <= 0       */
 #define KVQ_ELAYOUT (-2)   /* layout id is not KVQ_LAYOUT_V41 / KVQ_LAYOUT_V41_FP4 */
-#define KVQ_ERATIO (-3)    /* compression ratio not built (supported: 1, 2, 4, 128) */
+#define KVQ_ERATIO (-3)    /* ratio not built (supported: 1, 2, 4, 8, 16, 32, 64, 128) */
 #define KVQ_ECAPACITY (-4) /* kv_translate_slots with n > cap; nothing enqueued   */
 #define KVQ_ELAUNCH (-5)   /* the HIP runtime rejected the kernel launch          */
 
@@ -115,7 +115,7 @@ int kv_store_rope(int32_t layout, void* pool, int64_t num_pages, const uint16_t*
  * ratio 1 is the identity (score is not read).
  *   kv, score  device fp32, row j at base + j*ld, R*ratio rows; 16-byte aligned
  *   ld         row stride in elements, >= 512 and a multiple of 4
- *   ratio      1, 2, 4 or 128 (others: KVQ_ERATIO)
+ *   ratio      1, 2, 4, 8, 16, 32, 64 or 128 (others: KVQ_ERATIO)
  *   pos, slots device int32[R]
  * Compressed codes may differ from an exact (float64) evaluation by at most one code
  * step where the fp32 pooled value rounds to a different bf16. */

@@ -24,7 +24,7 @@ V41_FP4 = 2
 HEAD_DIM = 512
 ROPE_DIM = 64
 PAGE_ROWS = 64
-SUPPORTED_RATIOS = (1, 2, 4, 128)
+SUPPORTED_RATIOS = (1, 2, 4, 8, 16, 32, 64, 128)
 
 KVQ_OK, KVQ_EINVAL, KVQ_ELAYOUT, KVQ_ERATIO, KVQ_ECAPACITY, KVQ_ELAUNCH = 0, -1, -2, -3, -4, -5
 

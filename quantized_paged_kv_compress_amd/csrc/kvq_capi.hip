@@ -18,6 +18,7 @@ namespace {
 using kvq::Layout;
 
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+constexpr int64_t kDequantLongList = 1024;  // pages; from here on 4 rows per wavefront
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -83,6 +84,10 @@ int compress_dispatch(int32_t ratio, void* pool, int64_t num_pages, const float*
         case 1: return compress_short<L, 1>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
         case 2: return compress_short<L, 2>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
         case 4: return compress_short<L, 4>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 8: return compress_long<L, 8, 4, 1>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 16: return compress_long<L, 16, 4, 2>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 32: return compress_long<L, 32, 4, 4>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 64: return compress_long<L, 64, 4, 4>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
         case 128: return compress_long<L, 128, 4, 4>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
         default: return KVQ_ERATIO;
     }
@@ -97,7 +102,7 @@ const char* kvq_status_string(int status) {
         case KVQ_OK: return "ok";
         case KVQ_EINVAL: return "invalid argument (null pointer, stride, alignment or size)";
         case KVQ_ELAYOUT: return "unknown layout id";
-        case KVQ_ERATIO: return "compression ratio not supported (1, 2, 4, 128)";
+        case KVQ_ERATIO: return "compression ratio not supported (1, 2, 4, 8, 16, 32, 64, 128)";
         case KVQ_ECAPACITY: return "more slots than the translation buffer holds";
         case KVQ_ELAUNCH: return "kernel launch rejected by the HIP runtime";
         default: return "unknown status";
@@ -159,7 +164,9 @@ int kv_compress_store(int32_t layout, void* pool, int64_t num_pages, const float
                       const float* cos_sin, int64_t max_pos, const int32_t* slots, int64_t R,
                       void* stream) {
     if (!known_layout(layout)) return KVQ_ELAYOUT;
-    if (ratio != 1 && ratio != 2 && ratio != 4 && ratio != 128) return KVQ_ERATIO;
+    if (ratio != 1 && ratio != 2 && ratio != 4 && ratio != 8 && ratio != 16 && ratio != 32 &&
+        ratio != 64 && ratio != 128)
+        return KVQ_ERATIO;
     if (R < 0 || R > kMaxRows || num_pages < 0 || max_pos <= 0) return KVQ_EINVAL;
     if (R == 0) return KVQ_OK;
     if (!pool || !kv || (ratio > 1 && !score) || !pos || !cos_sin || !slots) return KVQ_EINVAL;
@@ -178,11 +185,19 @@ int kv_dequant(int32_t layout, const void* pool, int64_t num_pages, const int32_
     if (P == 0) return KVQ_OK;
     if (!pool || !page_ids || !out) return KVQ_EINVAL;
     if (!aligned16(pool) || !aligned16(out)) return KVQ_EINVAL;
-    const dim3 grid(blocks_for(P << kvq::kPageBits, kvq::kRowsPerBlock)), block(kvq::kWave * kvq::kRowsPerBlock);
     const auto* p = static_cast<const uint8_t*>(pool);
+    const dim3 block(kvq::kWave * kvq::kRowsPerBlock);
+    const int64_t rows = P << kvq::kPageBits;
+    if (P >= kDequantLongList) {  // 4 rows per wavefront
+        const dim3 grid(blocks_for(rows, 4 * kvq::kRowsPerBlock));
+        if (layout == KVQ_LAYOUT_V41)
+            return launch(kvq::dequant_kernel<Layout::V41, 4>, grid, block, stream, p, num_pages, page_ids, P, out);
+        return launch(kvq::dequant_kernel<Layout::V41_FP4, 4>, grid, block, stream, p, num_pages, page_ids, P, out);
+    }
+    const dim3 grid(blocks_for(rows, kvq::kRowsPerBlock));
     if (layout == KVQ_LAYOUT_V41)
-        return launch(kvq::dequant_kernel<Layout::V41>, grid, block, stream, p, num_pages, page_ids, P, out);
-    return launch(kvq::dequant_kernel<Layout::V41_FP4>, grid, block, stream, p, num_pages, page_ids, P, out);
+        return launch(kvq::dequant_kernel<Layout::V41, 1>, grid, block, stream, p, num_pages, page_ids, P, out);
+    return launch(kvq::dequant_kernel<Layout::V41_FP4, 1>, grid, block, stream, p, num_pages, page_ids, P, out);
 }
 
 int kv_translate_slots(const int32_t* table, int64_t table_len, const int32_t* full_loc, int64_t n,

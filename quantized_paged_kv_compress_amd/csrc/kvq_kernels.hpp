@@ -221,56 +221,73 @@ __global__ __launch_bounds__(kWave * kWaves) void compress_long_kernel(
 }
 
 // ------------------------------------------------------------------ dequant
-// One wavefront per output row (page p of the list, row r): lane l reads its 8 codes
-// and the scale byte of its block, and writes 8 bf16 (16 B).
-template <Layout L>
+// Each wavefront dequantises kRowsPerWave consecutive rows of one listed page: lane l
+// reads its 8 codes and the scale byte of its block for every row (all loads issued
+// before any use), then writes 8 bf16 (16 B) per row.  One row per wavefront suits
+// short page lists (more wavefronts to spread the launch); longer lists use 4 rows per
+// wavefront to keep more bytes in flight per wavefront.
+template <Layout L, int kRowsPerWave>
 __global__ __launch_bounds__(kWave * kRowsPerBlock) void dequant_kernel(
     const uint8_t* __restrict__ pool, int64_t num_pages, const int32_t* __restrict__ page_ids,
     int64_t P, uint16_t* __restrict__ out) {
     using T = LayoutTraits<L>;
+    static_assert((1 << kPageBits) % kRowsPerWave == 0, "a wavefront stays inside one page");
     constexpr int64_t kPB = kv_page_bytes<L>(1 << kPageBits);
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t g = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave_id();
-    if (g >= P * (1 << kPageBits)) return;
-    const int32_t page = page_ids[g >> kPageBits];
+    const int64_t g0 = (static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave_id()) * kRowsPerWave;
+    if (g0 >= P * (1 << kPageBits)) return;
+    const int32_t page = page_ids[g0 >> kPageBits];
     if (page < 0 || page >= num_pages) return;
-    const int row = static_cast<int>(g & ((1 << kPageBits) - 1));
+    const int row0 = static_cast<int>(g0 & ((1 << kPageBits) - 1));
     const uint8_t* pg = pool + static_cast<int64_t>(page) * kPB;
-    const uint8_t* code_row = pg + row * T::kCodeRowBytes;
-    const uint32_t sb = pg[(int64_t(1) << kPageBits) * T::kCodeRowBytes + row * T::kScaleRowBytes + (lane >> 2)];
 
-    uint32_t o[8];
-    if constexpr (L == Layout::V41) {
-        const uint2 cw = *reinterpret_cast<const uint2*>(code_row + kElemsPerLane * lane);
-        const int k = static_cast<int>(sb) - 127;
+    uint32_t cw[kRowsPerWave][2], sb[kRowsPerWave];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t c = ((e < 4 ? cw.x : cw.y) >> (8 * (e & 3))) & 0xFFu;
-            const uint32_t mag = c & 0x7Fu;
-            const float val = __builtin_amdgcn_ldexpf(e4m3_mag_value(mag), k);  // exact unless it
-            uint32_t b = bf16_rne_bits(val) | ((c & 0x80u) << 8);               // under/overflows
-            if (mag == 0x7Fu || sb == 0xFFu) b = 0x7FC0u;
-            o[e] = b;
+    for (int r = 0; r < kRowsPerWave; ++r) {
+        const uint8_t* code_row = pg + (row0 + r) * T::kCodeRowBytes;
+        if constexpr (L == Layout::V41) {
+            const uint2 c = *reinterpret_cast<const uint2*>(code_row + kElemsPerLane * lane);
+            cw[r][0] = c.x;
+            cw[r][1] = c.y;
+        } else {
+            cw[r][0] = *reinterpret_cast<const uint32_t*>(code_row + T::kCodeBytesPerLane * lane);
+            cw[r][1] = 0;
         }
-    } else {
-        const uint32_t cw = *reinterpret_cast<const uint32_t*>(code_row + T::kCodeBytesPerLane * lane);
-        const bool nan_scale = (sb & 0x7Fu) == 0x7Fu;
-        const float s = (sb & 0x80u) ? -e4m3_mag_value(sb & 0x7Fu) : e4m3_mag_value(sb & 0x7Fu);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t nib = (cw >> (4 * e)) & 0xFu;
-            const uint32_t ex = (nib >> 1) & 3u, mb = nib & 1u;
-            const float mag = ex ? __uint_as_float(((ex + 126u) << 23) | (mb << 22)) : 0.5f * static_cast<float>(mb);
-            const float val = ((nib & 8u) ? -mag : mag) * s;  // exact: at most 5 significant bits
-            o[e] = nan_scale ? 0x7FC0u : bf16_rne_bits(val);
-        }
+        sb[r] = pg[(int64_t(1) << kPageBits) * T::kCodeRowBytes + (row0 + r) * T::kScaleRowBytes + (lane >> 2)];
     }
-    uint4 st;
-    st.x = o[0] | (o[1] << 16);
-    st.y = o[2] | (o[3] << 16);
-    st.z = o[4] | (o[5] << 16);
-    st.w = o[6] | (o[7] << 16);
-    *reinterpret_cast<uint4*>(out + g * kHeadDim + kElemsPerLane * lane) = st;
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+        uint32_t o[8];
+        if constexpr (L == Layout::V41) {
+            const int k = static_cast<int>(sb[r]) - 127;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t c = (cw[r][e >> 2] >> (8 * (e & 3))) & 0xFFu;
+                const uint32_t mag = c & 0x7Fu;
+                const float val = __builtin_amdgcn_ldexpf(e4m3_mag_value(mag), k);  // exact unless it
+                uint32_t b = bf16_rne_bits(val) | ((c & 0x80u) << 8);               // under/overflows
+                if (mag == 0x7Fu || sb[r] == 0xFFu) b = 0x7FC0u;
+                o[e] = b;
+            }
+        } else {
+            const bool nan_scale = (sb[r] & 0x7Fu) == 0x7Fu;
+            const float s = (sb[r] & 0x80u) ? -e4m3_mag_value(sb[r] & 0x7Fu) : e4m3_mag_value(sb[r] & 0x7Fu);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t nib = (cw[r][0] >> (4 * e)) & 0xFu;
+                const uint32_t ex = (nib >> 1) & 3u, mb = nib & 1u;
+                const float mag = ex ? __uint_as_float(((ex + 126u) << 23) | (mb << 22)) : 0.5f * static_cast<float>(mb);
+                const float val = ((nib & 8u) ? -mag : mag) * s;  // exact: at most 5 significant bits
+                o[e] = nan_scale ? 0x7FC0u : bf16_rne_bits(val);
+            }
+        }
+        uint4 st;
+        st.x = o[0] | (o[1] << 16);
+        st.y = o[2] | (o[3] << 16);
+        st.z = o[4] | (o[5] << 16);
+        st.w = o[6] | (o[7] << 16);
+        *reinterpret_cast<uint4*>(out + (g0 + r) * kHeadDim + kElemsPerLane * lane) = st;
+    }
 }
 
 // ------------------------------------------------------------------ full -> SWA slots

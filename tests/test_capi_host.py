@@ -102,7 +102,7 @@ def test_compress_argument_checks(kvq):
         args = dict(zip(names, ok))
         args.update(kw)
         return L.kv_compress_store(*[args[n] for n in names])
-    for r in (0, 3, 5, 8, 64, 129, -4):
+    for r in (0, 3, 5, 6, 12, 96, 129, 256, -4):
         assert call(ratio=r) == kvq.KVQ_ERATIO
     assert call(layout=0) == kvq.KVQ_ELAYOUT
     assert call(R=0) == kvq.KVQ_OK

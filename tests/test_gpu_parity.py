@@ -205,7 +205,8 @@ def test_compress_ratio1_is_bit_exact(kvq, orc, cos_sin, cos_sin_dev, layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("ratio,R", [(2, 515), (4, 1001), (4, 3), (128, 37), (128, 1)])
+@pytest.mark.parametrize("ratio,R", [(2, 515), (4, 1001), (4, 3), (8, 301), (16, 150), (32, 99),
+                                     (64, 45), (128, 37), (128, 1)])
 def test_compress_small_within_tolerance(kvq, orc, cos_sin, cos_sin_dev, layout, ratio, R):
     rng = np.random.default_rng(1000 * ratio + R)
     num_pages = max(4, (R + 63) // 64 * 2)
@@ -343,6 +344,23 @@ def test_dequant_after_store_bit_exact(kvq, orc, layout):
     pages = np.unique(slots >> 6).astype(np.int32)[::-1].copy()     # any order
     out = kvq.kv_dequant(pool, layout, to_dev(pages))
     ref = orc.kv_dequant(layout, to_host(pool), pages)
+    assert np.array_equal(to_host(out), ref)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_dequant_long_page_list_bit_exact(kvq, orc, layout):
+    """Lists of 1024 pages or more use four rows per wavefront; random pool bytes (NaN
+    codes and scales included), repeated and out-of-pool page ids."""
+    rng = np.random.default_rng(16)
+    num_pages = 1500
+    pool = rng.integers(0, 256, (num_pages, kvq.page_bytes(layout))).astype(np.uint8)
+    pages = rng.integers(0, num_pages, 1100).astype(np.int32)
+    pages[[3, 500, 1099]] = [-1, num_pages, 7]
+    import torch
+    out = torch.full((pages.size * 64, 512), 0x2468, dtype=torch.int16, device="cuda")
+    kvq.kv_dequant(to_dev(pool), layout, to_dev(pages), out)
+    ref = np.full((pages.size * 64, 512), 0x2468, np.uint16)
+    orc.kv_dequant(layout, pool, pages, ref)
     assert np.array_equal(to_host(out), ref)
 
 
