@@ -84,7 +84,8 @@ def read_traffic(duration_key_bytes):
 
 def micro_bench(kvq, wl, dev, cs, layers=61, reps=20, calls=50):
     """Graph-replayed per-launch latency of the kernels in P1's latency table (store,
-    store+RoPE, c1, c2 at 1/8/64/512 tokens, V41, hot inputs), and the P2 hoisting case:
+    store+RoPE, fused K norm+RoPE, c1, c2 at 1/8/64/512 tokens, V41, hot inputs), and the
+    P2 hoisting case:
     one full->SWA translation reused by `layers` per-layer store+RoPE calls, against a
     translation inside every layer."""
     import numpy as np
@@ -121,6 +122,7 @@ def micro_bench(kvq, wl, dev, cs, layers=61, reps=20, calls=50):
     rng = np.random.default_rng(123)
     num_pages = 4096
     pool = kvq.new_pool(kvq.V41, num_pages)
+    w = t(wl.bf16_bits(rng.uniform(0.5, 1.5, HEAD).astype(np.float32)))
     table = {}
     for bs in (1, 8, 64, 512):
         k = t(wl.bf16_bits(rng.standard_normal((bs, HEAD)).astype(np.float32)))
@@ -131,6 +133,7 @@ def micro_bench(kvq, wl, dev, cs, layers=61, reps=20, calls=50):
         fns = {
             "store": lambda: kvq.kv_store(pool, kvq.V41, k, slots),
             "store_rope": lambda: kvq.kv_store_rope(pool, kvq.V41, k, pos, cs, slots),
+            "k_norm_rope": lambda: kvq.kv_store_norm_rope(pool, kvq.V41, k, w, 1e-6, pos, cs, slots),
             "c1": lambda: kvq.kv_compress_store(pool, kvq.V41, kv[:bs], None, 1, pos, cs, slots),
             "c2": lambda: kvq.kv_compress_store(pool, kvq.V41, kv, sc, 2, pos, cs, slots),
         }

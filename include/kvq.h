@@ -107,6 +107,20 @@ int kv_store_rope(int32_t layout, void* pool, int64_t num_pages, const uint16_t*
                   int64_t ld, const int32_t* pos, const float* cos_sin, int64_t max_pos,
                   const int32_t* slots, int64_t n, void* stream);
 
+/* kv_store_norm_rope -- the fused "K norm + RoPE" store of [P1]'s latency table.  The
+ * page gives no formula; this library reads it as RMS normalisation of the whole row with
+ * a per-channel weight, y_c = bf16(x_c * w_c / sqrt(mean_c(x_c^2) + eps)) (computed in
+ * fp32), followed by kv_store_rope on y.
+ *   weight     device bf16 bits [512], 16-byte aligned
+ *   eps        >= 0 and finite (else KVQ_EINVAL)
+ * Other arguments as kv_store_rope.  y may differ from an exact (float64) evaluation by
+ * one bf16 step where the fp32 result rounds the other way, so codes may differ by at
+ * most one step from such an evaluation. */
+int kv_store_norm_rope(int32_t layout, void* pool, int64_t num_pages, const uint16_t* k,
+                       int64_t ld, const uint16_t* weight, float eps, const int32_t* pos,
+                       const float* cos_sin, int64_t max_pos, const int32_t* slots, int64_t n,
+                       void* stream);
+
 /* kv_compress_store -- the c1 / C4A / C128A compressors ([P3] sections 1-3; [P1]
  * section 2).  Output row i pools input rows [i*ratio, i*ratio + ratio) channel by
  * channel: weights are the softmax over the window of score[.][c], the pooled value is

@@ -23,6 +23,10 @@ e2m1 / fp4 scale  P1 s.1-2 (e2m1 codes, e4m3 scale per 32)  exhaustive vs brute 
                                                             with exact rational ties
 RoPE              P3 s.3; NeoX half rotation                pos 0 identity; hand-computed
                                                             angles; norm preservation
+K norm (RMS)      P1 latency table "fused K norm + RoPE"    hand-computed row (eps 0);
+                  (formula is a reading)                    power-of-two scale invariance;
+                                                            weight channel mapping;
+                                                            Python fsum brute force
 pooling           P3 s.2 (per-channel online softmax)       r = 1 identity; equal scores
                                                             give the mean; dominance;
                                                             permutation and shift
@@ -105,6 +109,8 @@ def _load(path):
         "orc_kv_store": (ctypes.c_int, [i32, vp, i64, vp, i64, vp, i64]),
         "orc_kv_store_rope": (ctypes.c_int, [i32, vp, i64, vp, i64, vp, vp, i64, vp, i64]),
         "orc_pool_rows": (ctypes.c_int, [vp, vp, i64, i32, i64, vp, vp]),
+        "orc_kv_store_norm_rope": (ctypes.c_int, [i32, vp, i64, vp, i64, vp, f32, vp, vp, i64, vp, i64]),
+        "orc_norm_row": (ctypes.c_int, [vp, vp, f32]),
         "orc_kv_compress_store": (ctypes.c_int,
                                   [i32, vp, i64, vp, vp, i64, i32, vp, vp, i64, vp, i64]),
         "orc_kv_dequant": (ctypes.c_int, [i32, vp, i64, vp, i64, vp]),
@@ -234,6 +240,28 @@ def kv_store_rope(layout, pool, k_bf16, pos, cos_sin, slots):
     _ok(lib().orc_kv_store_rope(layout, _p(pool), pool.shape[0], _p(k_bf16), k_bf16.shape[1],
                                 _p(pos), _p(cos_sin), cos_sin.shape[0], _p(slots), n),
         "kv_store_rope")
+
+
+def norm_row(v_bf16, weight_bf16, eps):
+    v = np.array(v_bf16, dtype=np.uint16, copy=True)
+    w = np.ascontiguousarray(weight_bf16, dtype=np.uint16)
+    assert v.shape == (HEAD,) and w.shape == (HEAD,)
+    _ok(lib().orc_norm_row(_p(v), _p(w), float(eps)), "norm_row")
+    return v
+
+
+def kv_store_norm_rope(layout, pool, k_bf16, weight_bf16, eps, pos, cos_sin, slots):
+    _check(pool, np.uint8, "pool")
+    _check(k_bf16, np.uint16, "k")
+    _check(weight_bf16, np.uint16, "weight")
+    _check(pos, np.int32, "pos")
+    _check(cos_sin, np.float32, "cos_sin")
+    _check(slots, np.int32, "slots")
+    n = slots.shape[0]
+    assert pos.shape[0] == n and weight_bf16.shape == (HEAD,)
+    _ok(lib().orc_kv_store_norm_rope(layout, _p(pool), pool.shape[0], _p(k_bf16), k_bf16.shape[1],
+                                     _p(weight_bf16), float(eps), _p(pos), _p(cos_sin),
+                                     cos_sin.shape[0], _p(slots), n), "kv_store_norm_rope")
 
 
 def pool_rows(kv, score, ratio):

@@ -293,6 +293,46 @@ int orc_kv_store_rope(int32_t layout, uint8_t* pool, int64_t num_pages, const ui
     return 0;
 }
 
+/* ---------------------------------------------------------------- K norm + RoPE */
+/* The "fused K norm + RoPE" store of [P1]'s latency table; the page gives no formula.
+ * Reading: RMS normalisation of the whole 512-channel bf16 row with a per-channel weight,
+ * y_c = x_c * w_c / sqrt(mean_c(x_c^2) + eps), evaluated in float64 and rounded once to
+ * bf16; then RoPE and the store as in orc_kv_store_rope. */
+static void norm_row(float* v, const uint16_t* w_bf16, float eps) {
+    double ss = 0.0;
+    for (int c = 0; c < kHead; c++) ss += (double)v[c] * (double)v[c];
+    double r = 1.0 / sqrt(ss / kHead + (double)eps);
+    for (int c = 0; c < kHead; c++)
+        v[c] = orc_bf16_to_f32(orc_bf16_from_double((double)v[c] * (double)orc_bf16_to_f32(w_bf16[c]) * r));
+}
+
+int orc_kv_store_norm_rope(int32_t layout, uint8_t* pool, int64_t num_pages, const uint16_t* k,
+                           int64_t ld, const uint16_t* weight, float eps, const int32_t* pos,
+                           const float* cos_sin, int64_t max_pos, const int32_t* slots, int64_t n) {
+    if (orc_bytes_per_token(layout) < 0) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) {
+        uint8_t *code, *scale;
+        if (!row_address(layout, pool, num_pages, slots[i], &code, &scale)) continue;
+        if (pos[i] < 0 || pos[i] >= max_pos) continue;
+        float v[512];
+        for (int c = 0; c < kHead; c++) v[c] = orc_bf16_to_f32(k[i * ld + c]);
+        norm_row(v, weight, eps);
+        rope_row(v, cos_sin + (int64_t)pos[i] * kRopeDim);
+        quant_row(layout, v, code, scale);
+    }
+    return 0;
+}
+
+/* Normalised row only (for the pins): bf16 bits of y. */
+int orc_norm_row(uint16_t* v_bf16, const uint16_t* weight, float eps) {
+    float v[512];
+    for (int c = 0; c < kHead; c++) v[c] = orc_bf16_to_f32(v_bf16[c]);
+    norm_row(v, weight, eps);
+    for (int c = 0; c < kHead; c++) v_bf16[c] = orc_bf16_from_double((double)v[c]);
+    return 0;
+}
+
 /* ---------------------------------------------------------------- pooling */
 /* Softmax pooling of window i ([P3] section 2): for every channel c, the weights are the
  * softmax over the r window rows of the scores in that channel, and the pooled value is

@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "V41", "V41_FP4", "KVQError", "load_library", "bytes_per_token", "page_bytes",
-    "code_row_bytes", "scale_row_bytes", "new_pool", "kv_store", "kv_store_rope",
+    "code_row_bytes", "scale_row_bytes", "new_pool", "kv_store", "kv_store_rope", "kv_store_norm_rope",
     "kv_compress_store", "kv_dequant", "kv_translate_slots", "SUPPORTED_RATIOS",
 ]
 
@@ -56,6 +56,7 @@ def load_library() -> ctypes.CDLL:
     sigs = {
         "kv_store": [i32, vp, i64, vp, i64, vp, i64, vp],
         "kv_store_rope": [i32, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp],
+        "kv_store_norm_rope": [i32, vp, i64, vp, i64, vp, ctypes.c_float, vp, vp, i64, vp, i64, vp],
         "kv_compress_store": [i32, vp, i64, vp, vp, i64, i32, vp, vp, i64, vp, i64, vp],
         "kv_dequant": [i32, vp, i64, vp, i64, vp, vp],
         "kv_translate_slots": [vp, i64, vp, i64, vp, i64, vp],
@@ -164,6 +165,27 @@ def kv_store_rope(pool, layout, k, pos, cos_sin, slots, stream=None):
     _raise("kv_store_rope", load_library().kv_store_rope(
         layout, _ptr(pool), num_pages, _ptr(k), ld, _ptr(pos), _ptr(cos_sin), cos_sin.shape[0],
         _ptr(slots), n, _stream(stream)))
+
+
+def kv_store_norm_rope(pool, layout, k, weight, eps, pos, cos_sin, slots, stream=None):
+    """RMS-normalise each row with a per-channel bf16 weight, RoPE at pos[i], quantise into
+    slots[i]."""
+    num_pages = _pool(pool, layout)
+    ld = _rows(_dev(k, "k", _BF16), "k")
+    _dev(weight, "weight", _BF16)
+    if not weight.is_contiguous() or weight.numel() != HEAD_DIM:
+        raise ValueError("weight: need a contiguous bf16 [512] tensor")
+    _dev(pos, "pos", _I32)
+    _dev(slots, "slots", _I32)
+    _dev(cos_sin, "cos_sin", _F32)
+    if not cos_sin.is_contiguous() or cos_sin.dim() != 2 or cos_sin.shape[1] != ROPE_DIM:
+        raise ValueError("cos_sin: need a contiguous fp32 [max_pos, 64] tensor")
+    n = slots.numel()
+    if k.shape[0] < n or pos.numel() != n:
+        raise ValueError("k / pos / slots sizes disagree")
+    _raise("kv_store_norm_rope", load_library().kv_store_norm_rope(
+        layout, _ptr(pool), num_pages, _ptr(k), ld, _ptr(weight), float(eps), _ptr(pos),
+        _ptr(cos_sin), cos_sin.shape[0], _ptr(slots), n, _stream(stream)))
 
 
 def kv_compress_store(pool, layout, kv, score, ratio, pos, cos_sin, slots, stream=None):

@@ -45,17 +45,20 @@ unsigned blocks_for(int64_t rows, int per_block) {
 }
 
 template <Layout L>
-int store_impl(bool rope, void* pool, int64_t num_pages, const uint16_t* k, int64_t ld,
-               const int32_t* pos, const float* cos_sin, int64_t max_pos, const int32_t* slots,
-               int64_t n, void* stream) {
+int store_impl(int mode, void* pool, int64_t num_pages, const uint16_t* k, int64_t ld,
+               const uint16_t* weight, float eps, const int32_t* pos, const float* cos_sin,
+               int64_t max_pos, const int32_t* slots, int64_t n, void* stream) {
     const dim3 grid(blocks_for(n, kvq::kRowsPerBlock)), block(kvq::kWave * kvq::kRowsPerBlock);
     const int64_t nslots = num_pages << kvq::kPageBits;
     auto* p = static_cast<uint8_t*>(pool);
-    if (rope)
-        return launch(kvq::store_kernel<L, true>, grid, block, stream, p, nslots, k, ld, pos,
-                      cos_sin, max_pos, slots, n);
-    return launch(kvq::store_kernel<L, false>, grid, block, stream, p, nslots, k, ld, pos,
-                  cos_sin, max_pos, slots, n);
+    if (mode == 2)
+        return launch(kvq::store_kernel<L, true, true>, grid, block, stream, p, nslots, k, ld, weight,
+                      eps, pos, cos_sin, max_pos, slots, n);
+    if (mode == 1)
+        return launch(kvq::store_kernel<L, true, false>, grid, block, stream, p, nslots, k, ld, weight,
+                      eps, pos, cos_sin, max_pos, slots, n);
+    return launch(kvq::store_kernel<L, false, false>, grid, block, stream, p, nslots, k, ld, weight,
+                  eps, pos, cos_sin, max_pos, slots, n);
 }
 
 template <Layout L, int kRatio>
@@ -133,30 +136,46 @@ int64_t kvq_page_bytes(int32_t layout) {
     return KVQ_ELAYOUT;
 }
 
-static int store_common(bool rope, int32_t layout, void* pool, int64_t num_pages, const uint16_t* k,
-                        int64_t ld, const int32_t* pos, const float* cos_sin, int64_t max_pos,
-                        const int32_t* slots, int64_t n, void* stream) {
+// mode 0: plain store, 1: RoPE, 2: RMS norm + RoPE
+static int store_common(int mode, int32_t layout, void* pool, int64_t num_pages, const uint16_t* k,
+                        int64_t ld, const uint16_t* weight, float eps, const int32_t* pos,
+                        const float* cos_sin, int64_t max_pos, const int32_t* slots, int64_t n,
+                        void* stream) {
+    const bool rope = mode >= 1, norm = mode == 2;
     if (!known_layout(layout)) return KVQ_ELAYOUT;
     if (n < 0 || n > kMaxRows || num_pages < 0) return KVQ_EINVAL;
     if (rope && max_pos <= 0) return KVQ_EINVAL;
+    if (norm && !(eps >= 0.0f && eps < __builtin_huge_valf())) return KVQ_EINVAL;
     if (n == 0) return KVQ_OK;
-    if (!pool || !k || !slots || (rope && (!pos || !cos_sin))) return KVQ_EINVAL;
+    if (!pool || !k || !slots || (rope && (!pos || !cos_sin)) || (norm && !weight)) return KVQ_EINVAL;
     if (ld < kvq::kHeadDim || ld % 8 != 0) return KVQ_EINVAL;
-    if (!aligned16(pool) || !aligned16(k) || (rope && !aligned16(cos_sin))) return KVQ_EINVAL;
+    if (!aligned16(pool) || !aligned16(k) || (rope && !aligned16(cos_sin)) || (norm && !aligned16(weight)))
+        return KVQ_EINVAL;
     if (layout == KVQ_LAYOUT_V41)
-        return store_impl<Layout::V41>(rope, pool, num_pages, k, ld, pos, cos_sin, max_pos, slots, n, stream);
-    return store_impl<Layout::V41_FP4>(rope, pool, num_pages, k, ld, pos, cos_sin, max_pos, slots, n, stream);
+        return store_impl<Layout::V41>(mode, pool, num_pages, k, ld, weight, eps, pos, cos_sin, max_pos,
+                                       slots, n, stream);
+    return store_impl<Layout::V41_FP4>(mode, pool, num_pages, k, ld, weight, eps, pos, cos_sin, max_pos,
+                                       slots, n, stream);
 }
 
 int kv_store(int32_t layout, void* pool, int64_t num_pages, const uint16_t* k, int64_t ld,
              const int32_t* slots, int64_t n, void* stream) {
-    return store_common(false, layout, pool, num_pages, k, ld, nullptr, nullptr, 1, slots, n, stream);
+    return store_common(0, layout, pool, num_pages, k, ld, nullptr, 0.0f, nullptr, nullptr, 1, slots, n,
+                        stream);
 }
 
 int kv_store_rope(int32_t layout, void* pool, int64_t num_pages, const uint16_t* k, int64_t ld,
                   const int32_t* pos, const float* cos_sin, int64_t max_pos, const int32_t* slots,
                   int64_t n, void* stream) {
-    return store_common(true, layout, pool, num_pages, k, ld, pos, cos_sin, max_pos, slots, n, stream);
+    return store_common(1, layout, pool, num_pages, k, ld, nullptr, 0.0f, pos, cos_sin, max_pos, slots, n,
+                        stream);
+}
+
+int kv_store_norm_rope(int32_t layout, void* pool, int64_t num_pages, const uint16_t* k, int64_t ld,
+                       const uint16_t* weight, float eps, const int32_t* pos, const float* cos_sin,
+                       int64_t max_pos, const int32_t* slots, int64_t n, void* stream) {
+    return store_common(2, layout, pool, num_pages, k, ld, weight, eps, pos, cos_sin, max_pos, slots, n,
+                        stream);
 }
 
 int kv_compress_store(int32_t layout, void* pool, int64_t num_pages, const float* kv,

@@ -146,6 +146,37 @@ __device__ __forceinline__ void rope_apply(float (&v)[8], const RopeCS& cs, int 
     }
 }
 
+// ---------------------------------------------------------------- K norm (RMS)
+// Sum of a float over the whole wavefront, in a fixed order: quad, pairs of quads and
+// the 16-lane DPP row by DPP adds, then the four rows through readlane.  Every lane gets
+// the same value.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += __uint_as_float(dpp<0xB1>(__float_as_uint(v)));
+    v += __uint_as_float(dpp<0x4E>(__float_as_uint(v)));
+    v += __uint_as_float(dpp<0x124>(__float_as_uint(v)));   // row_ror:4
+    v += __uint_as_float(dpp<0x128>(__float_as_uint(v)));   // row_ror:8
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (a + b) + (c + d);
+}
+
+// RMS normalisation of a row with a per-channel bf16 weight (the "fused K norm + RoPE"
+// store of the sglang V41 page's latency table, read as y = x * w / sqrt(mean(x^2) + eps)),
+// in float32, results rounded to bf16.  Every lane must call this.
+__device__ __forceinline__ void rms_norm_row(float (&v)[8], const uint16_t* __restrict__ weight, float eps,
+                                             int lane) {
+    float w[8];
+    load_row_bf16(weight, lane, w);
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(v[e], v[e], ss);
+    const float r = 1.0f / __builtin_sqrtf(wave_sum(ss) * (1.0f / kHeadDim) + eps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = round_bf16((v[e] * r) * w[e]);
+}
+
 // ---------------------------------------------------------------- quantise + store
 // Quantise this lane's 8 bf16-valued floats of a row and write its share of the row at
 // `slot` (the caller has checked the slot is inside the pool).  Every lane must call

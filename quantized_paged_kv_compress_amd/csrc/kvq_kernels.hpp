@@ -21,12 +21,14 @@ __device__ __forceinline__ int wave_id() {
 }
 
 // ------------------------------------------------------------------ store / store+RoPE
-// One wavefront per bf16 row: two 8-byte loads per lane, optional RoPE, quantise, store.
-template <Layout L, bool kRope>
+// One wavefront per bf16 row: two 8-byte loads per lane, optional RMS norm (kNorm, always
+// followed by RoPE), optional RoPE, quantise, store.
+template <Layout L, bool kRope, bool kNorm>
 __global__ __launch_bounds__(kWave * kRowsPerBlock) void store_kernel(
     uint8_t* __restrict__ pool, int64_t nslots, const uint16_t* __restrict__ k, int64_t ld,
-    const int32_t* __restrict__ pos, const float* __restrict__ cos_sin, int64_t max_pos,
-    const int32_t* __restrict__ slots, int64_t n) {
+    const uint16_t* __restrict__ weight, float eps, const int32_t* __restrict__ pos,
+    const float* __restrict__ cos_sin, int64_t max_pos, const int32_t* __restrict__ slots, int64_t n) {
+    static_assert(kRope || !kNorm, "the norm is fused with RoPE");
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t i = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave_id();
     if (i >= n) return;
@@ -40,6 +42,7 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void store_kernel(
     }
     float v[8];
     load_row_bf16(k + i * ld, lane, v);
+    if constexpr (kNorm) rms_norm_row(v, weight, eps, lane);
     if constexpr (kRope) rope_apply(v, cs, lane);
     quantize_store_row<L>(pool, static_cast<uint32_t>(slot), v, lane);
 }

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for want in ("kv_store", "kv_store_rope", "kv_compress_store", "kv_dequant",
+    for want in ("kv_store", "kv_store_rope", "kv_store_norm_rope", "kv_compress_store", "kv_dequant",
                  "kv_translate_slots", "kvq_bytes_per_token", "kvq_page_bytes"):
         assert want in names
 
@@ -91,6 +91,25 @@ def test_store_rope_argument_checks(kvq):
     assert L.kv_store_rope(V41, A, 4, B, 512, C, A + 4, 10, C, 1, None) == kvq.KVQ_EINVAL
     assert L.kv_store_rope(9, A, 4, B, 512, C, A, 10, C, 1, None) == kvq.KVQ_ELAYOUT
     assert L.kv_store_rope(FP4, A, 4, B, 512, C, A, 10, C, 0, None) == kvq.KVQ_OK
+
+
+def test_store_norm_rope_argument_checks(kvq):
+    L = kvq.load_library()
+    ok = dict(layout=V41, pool=A, num_pages=4, k=B, ld=512, w=C, eps=1e-6, pos=A, cs=B, max_pos=10,
+              slots=C, n=3, stream=None)
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.kv_store_norm_rope(*a.values())
+    assert call(n=0) == kvq.KVQ_OK
+    assert call(w=None) == kvq.KVQ_EINVAL
+    assert call(w=C + 8) == kvq.KVQ_EINVAL
+    assert call(eps=-1.0) == kvq.KVQ_EINVAL
+    assert call(eps=float("nan")) == kvq.KVQ_EINVAL
+    assert call(eps=float("inf")) == kvq.KVQ_EINVAL
+    assert call(max_pos=0) == kvq.KVQ_EINVAL
+    assert call(pos=None) == kvq.KVQ_EINVAL
+    assert call(layout=3) == kvq.KVQ_ELAYOUT
 
 
 def test_compress_argument_checks(kvq):

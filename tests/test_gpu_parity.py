@@ -176,6 +176,28 @@ def test_store_rope_edges(kvq, orc, cos_sin, cos_sin_dev, layout):
     assert np.array_equal(to_host(pool), ref)
 
 
+# ------------------------------------------------------------------ K norm + RoPE
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("n,eps", [(1, 1e-6), (130, 1e-6), (512, 0.0), (1001, 0.25)])
+def test_store_norm_rope_within_tolerance(kvq, orc, cos_sin, cos_sin_dev, layout, n, eps):
+    import torch
+    rng = np.random.default_rng(200 + n)
+    num_pages = max(8, (n + 63) // 64 * 2)
+    k = wl.bf16_bits((rng.standard_normal((n, 512)) * np.exp(rng.uniform(-4, 4, (n, 1)))).astype(np.float32))
+    w = wl.bf16_bits(rng.uniform(0.25, 2.0, 512).astype(np.float32))
+    pos = rng.integers(0, 65536, n).astype(np.int32)
+    slots = wl.distinct_slots(rng, n, 64, num_pages * 64)
+    pool, ref = canary_pool(kvq, layout, num_pages)
+    kvq.kv_store_norm_rope(pool, layout, to_dev(k), to_dev(w), eps, to_dev(pos), cos_sin_dev, to_dev(slots))
+    orc.kv_store_norm_rope(layout, ref, k, w, eps, pos, cos_sin, slots)
+    got = to_host(pool)
+    xv = (k.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    wv = (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    exact = xv * wv / np.sqrt((xv * xv).mean(axis=1, keepdims=True) + eps)
+    compare_compressed(got, ref, layout, slots, exact, label=f"norm n{n} L{layout}")
+    assert untouched_equal(got, ref, layout, slots)
+
+
 # ------------------------------------------------------------------ compressors
 def run_compress(kvq, orc, layout, ratio, kv, sc, pos, slots, num_pages, cos_sin, cos_sin_dev):
     pool = kvq.new_pool(layout, num_pages)

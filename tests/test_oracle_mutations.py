@@ -51,6 +51,10 @@ MUTATIONS = [
      ["dequant_worked", "dequant_v41"]),
     ("translate tail not zeroed", "for (int64_t i = n; i < cap; i++) out[i] = 0;",
      "for (int64_t i = n; i < cap; i++) out[i] = -1;", ["translate"]),
+    ("rms over 448 channels", "double r = 1.0 / sqrt(ss / kHead + (double)eps);",
+     "double r = 1.0 / sqrt(ss / 448 + (double)eps);", ["norm_worked", "norm_exact"]),
+    ("norm weight shifted a channel", "(double)orc_bf16_to_f32(w_bf16[c]) * r", "(double)orc_bf16_to_f32(w_bf16[(c + 1) % kHead]) * r",
+     ["norm_worked", "norm_mapping"]),
     ("fp4 padding not written", "memset(scale + kHead / kBlock, 0, 16); /* documented padding */",
      "(void)0; /* padding left as it was */", ["addressing"]),
 ]
@@ -75,6 +79,9 @@ PINS = {
     "dequant_worked": lambda o: pins.test_dequant_worked_examples(o, golden),
     "dequant_v41": lambda o: pins.test_dequant_exhaustive_v41(o),
     "translate": lambda o: pins.test_translate_semantics(o, golden),
+    "norm_worked": lambda o: pins.test_norm_worked_examples(o, golden),
+    "norm_exact": lambda o: pins.test_norm_is_nearest_bf16_of_exact_value(o),
+    "norm_mapping": lambda o: pins.test_norm_scale_invariance_and_weight_mapping(o),
 }
 
 

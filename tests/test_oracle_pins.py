@@ -744,3 +744,75 @@ def test_compress_equals_pool_then_store_rope(orc):
         for i in (3, 4):
             page, r = divmod(int(slots[i]), 64)
             assert np.all(a[page, r * CR:(r + 1) * CR] == 0)
+
+# ---------------------------------------------------------------- K norm (RMS)
+def _row_from_spec(spec, default):
+    v = np.full(512, default, np.float32)
+    for k_, h in spec.items():
+        if k_ == "all":
+            v[:] = float.fromhex(h)
+        else:
+            v[int(k_)] = float.fromhex(h)
+    return wl.bf16_bits(v)
+
+
+def test_norm_worked_examples(orc, golden):
+    for ex in golden("worked_examples.json")["k_norm"]:
+        x = _row_from_spec(ex["x"], 0.0)
+        w = _row_from_spec(ex["weight"], 1.0)
+        y = orc.norm_row(x, w, ex["eps"])
+        for c, h in ex["y_bf16"].items():
+            assert y[int(c)] == int(h, 16), ex["why"]
+        if "all" not in ex["x"]:
+            others = np.ones(512, bool)
+            others[[int(c) for c in ex["x"]]] = False
+            assert np.all(bf16_vals(y[others]) == 0)
+
+
+def test_norm_is_nearest_bf16_of_exact_value(orc):
+    rng = np.random.default_rng(51)
+    for _ in range(40):
+        x = wl.bf16_bits((rng.standard_normal(512) * np.exp(rng.uniform(-3, 3))).astype(np.float32))
+        w = wl.bf16_bits(rng.uniform(0.5, 2.0, 512).astype(np.float32))
+        eps = float(rng.choice([0.0, 1e-6, 0.5]))
+        y = bf16_vals(orc.norm_row(x, w, eps)).astype(np.float64)
+        xv = bf16_vals(x).astype(np.float64)
+        wv = bf16_vals(w).astype(np.float64)
+        r = 1.0 / math.sqrt(math.fsum(xv * xv) / 512 + eps)
+        exact = xv * wv * r
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(exact), 1e-300))) - 7)
+        assert np.all(np.abs(y - exact) <= 0.5 * ulp * (1 + 1e-12))
+
+
+def test_norm_scale_invariance_and_weight_mapping(orc):
+    rng = np.random.default_rng(52)
+    x = rng.standard_normal(512).astype(np.float32)
+    w = wl.bf16_bits(np.ones(512, np.float32))
+    y = orc.norm_row(wl.bf16_bits(x), w, 0.0)
+    for k in (-20, -3, 1, 7):        # a power-of-two scale of the row cancels exactly (eps 0)
+        assert np.array_equal(orc.norm_row(wl.bf16_bits(x * np.float32(2.0 ** k)), w, 0.0), y)
+    for j in (0, 255, 256, 447, 448, 511):
+        wj = np.zeros(512, np.float32)
+        wj[j] = 1.0
+        yj = orc.norm_row(wl.bf16_bits(x), wl.bf16_bits(wj), 0.0)
+        nz = np.nonzero(bf16_vals(yj))[0]
+        assert nz.tolist() == ([j] if x[j] != 0 else [])
+        assert yj[j] == y[j]
+
+
+def test_norm_rope_store_composes(orc):
+    rng = np.random.default_rng(53)
+    n, num_pages = 70, 4
+    k = wl.bf16_bits(rng.standard_normal((n, 512)).astype(np.float32))
+    w = wl.bf16_bits(rng.uniform(0.5, 1.5, 512).astype(np.float32))
+    cs = wl.rope_cos_sin(max_pos=512)
+    pos = rng.integers(0, 512, n).astype(np.int32)
+    pos[3] = 600                                         # skipped
+    slots = wl.distinct_slots(rng, n, 0, num_pages * 64)
+    normed = np.stack([orc.norm_row(k[i], w, 1e-6) for i in range(n)])
+    for layout in (V41, FP4):
+        a = orc.new_pool(layout, num_pages)
+        b = orc.new_pool(layout, num_pages)
+        orc.kv_store_norm_rope(layout, a, k, w, 1e-6, pos, cs, slots)
+        orc.kv_store_rope(layout, b, normed, pos, cs, slots)
+        assert np.array_equal(a, b)
