@@ -148,6 +148,15 @@ int kv_compress_store(int32_t layout, void* pool, int64_t num_pages, const float
 int kv_dequant(int32_t layout, const void* pool, int64_t num_pages, const int32_t* page_ids,
                int64_t P, uint16_t* out, void* stream);
 
+/* kv_dequant_slots -- the per-token form of kv_dequant: out[i*512 + c] is the
+ * dequantised value of channel c of the row at slots[i] (same arithmetic and NaN rule as
+ * kv_dequant); rows whose slot is outside [0, num_pages*64) are left untouched.  For a
+ * consumer that needs a gathered set of tokens rather than whole pages.
+ *   slots      device int32[n]
+ *   out        device bf16 bits, [n][512], 16-byte aligned */
+int kv_dequant_slots(int32_t layout, const void* pool, int64_t num_pages, const int32_t* slots,
+                     int64_t n, uint16_t* out, void* stream);
+
 /* kv_translate_slots -- full-pool -> SWA-pool slot translation, done once per step into
  * a preallocated buffer ([P2] sections 1-2):
  *   out[i] = table[full_loc[i]] for i < n (-1 when full_loc[i] is outside

@@ -36,6 +36,8 @@ addressing        P1 s.1 (PagedKV page/row/scale row)       brute-force tagged r
                                                             canaries on a 4-page pool
 dequant           P1 s.4                                    decode tables; quant(dequant)
                                                             idempotence; round-trip bound
+dequant by slot   P1 s.4 (per-token form)                   equals the matching rows of the
+                                                            page dequant; skips out-of-pool
 translate         P2 s.1                                    buffer semantics printed on
                                                             the page (zero tail, refusal)
 whole pipeline    --                                        parity unpinned beyond the
@@ -114,6 +116,7 @@ def _load(path):
         "orc_kv_compress_store": (ctypes.c_int,
                                   [i32, vp, i64, vp, vp, i64, i32, vp, vp, i64, vp, i64]),
         "orc_kv_dequant": (ctypes.c_int, [i32, vp, i64, vp, i64, vp]),
+        "orc_kv_dequant_slots": (ctypes.c_int, [i32, vp, i64, vp, i64, vp]),
         "orc_translate_slots": (ctypes.c_int, [vp, i64, vp, i64, vp, i64]),
     }
     for name, (res, args) in sig.items():
@@ -300,6 +303,18 @@ def kv_dequant(layout, pool, page_ids, out=None):
     _check(out, np.uint16, "out")
     _ok(lib().orc_kv_dequant(layout, _p(pool), pool.shape[0], _p(page_ids), P, _p(out)),
         "kv_dequant")
+    return out
+
+
+def kv_dequant_slots(layout, pool, slots, out=None):
+    _check(pool, np.uint8, "pool")
+    _check(slots, np.int32, "slots")
+    n = slots.shape[0]
+    if out is None:
+        out = np.zeros((n, HEAD), np.uint16)
+    _check(out, np.uint16, "out")
+    _ok(lib().orc_kv_dequant_slots(layout, _p(pool), pool.shape[0], _p(slots), n, _p(out)),
+        "kv_dequant_slots")
     return out
 
 

@@ -443,6 +443,34 @@ int orc_kv_dequant(int32_t layout, const uint8_t* pool, int64_t num_pages,
     return 0;
 }
 
+/* Token-gather dequant: row i of the output is the dequantised row at slots[i] (the
+ * per-token counterpart of [P1] section 4's page dequant); rows whose slot is outside the
+ * pool are left untouched. */
+int orc_kv_dequant_slots(int32_t layout, const uint8_t* pool, int64_t num_pages,
+                         const int32_t* slots, int64_t n, uint16_t* out) {
+    if (orc_bytes_per_token(layout) < 0) return -2;
+    int64_t cr = orc_code_row_bytes(layout), sr = orc_scale_row_bytes(layout);
+    int64_t pb = orc_page_bytes(layout);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) {
+        int64_t slot = slots[i];
+        if (slot < 0 || slot >= num_pages * kPageRows) continue;
+        const uint8_t* pg = pool + (slot / kPageRows) * pb;
+        int64_t r = slot % kPageRows;
+        const uint8_t* code = pg + r * cr;
+        const uint8_t* scale = pg + kPageRows * cr + r * sr;
+        for (int c = 0; c < kHead; c++) {
+            uint8_t q;
+            if (layout == ORC_LAYOUT_V41)
+                q = code[c];
+            else
+                q = (c % 2 == 0) ? (code[c / 2] & 15) : (code[c / 2] >> 4);
+            out[i * kHead + c] = dequant_value(layout, q, scale[c / kBlock]);
+        }
+    }
+    return 0;
+}
+
 /* ---------------------------------------------------------------- full -> SWA slots */
 /* [P2] section 1: the translation of full-pool slots into SWA-pool slots is done once per
  * step into a preallocated int32 buffer whose tail beyond n is zeroed; when n exceeds the

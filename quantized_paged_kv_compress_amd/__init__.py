@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "V41", "V41_FP4", "KVQError", "load_library", "bytes_per_token", "page_bytes",
     "code_row_bytes", "scale_row_bytes", "new_pool", "kv_store", "kv_store_rope", "kv_store_norm_rope",
-    "kv_compress_store", "kv_dequant", "kv_translate_slots", "SUPPORTED_RATIOS",
+    "kv_compress_store", "kv_dequant", "kv_dequant_slots", "kv_translate_slots", "SUPPORTED_RATIOS",
 ]
 
 V41 = 1
@@ -59,6 +59,7 @@ def load_library() -> ctypes.CDLL:
         "kv_store_norm_rope": [i32, vp, i64, vp, i64, vp, ctypes.c_float, vp, vp, i64, vp, i64, vp],
         "kv_compress_store": [i32, vp, i64, vp, vp, i64, i32, vp, vp, i64, vp, i64, vp],
         "kv_dequant": [i32, vp, i64, vp, i64, vp, vp],
+        "kv_dequant_slots": [i32, vp, i64, vp, i64, vp, vp],
         "kv_translate_slots": [vp, i64, vp, i64, vp, i64, vp],
     }
     for name, args in sigs.items():
@@ -221,6 +222,21 @@ def kv_dequant(pool, layout, page_ids, out=None, stream=None):
         raise ValueError("out: need a contiguous [P*64, 512] bf16 tensor")
     _raise("kv_dequant", load_library().kv_dequant(layout, _ptr(pool), num_pages, _ptr(page_ids),
                                                    P, _ptr(out), _stream(stream)))
+    return out
+
+
+def kv_dequant_slots(pool, layout, slots, out=None, stream=None):
+    """bf16 [n, 512]: the dequantised rows at slots[i] (rows of out-of-pool slots untouched)."""
+    num_pages = _pool(pool, layout)
+    _dev(slots, "slots", _I32)
+    n = slots.numel()
+    if out is None:
+        out = torch.empty((n, HEAD_DIM), dtype=torch.bfloat16, device=pool.device)
+    _dev(out, "out", _BF16)
+    if not out.is_contiguous() or out.numel() < n * HEAD_DIM:
+        raise ValueError("out: need a contiguous [n, 512] bf16 tensor")
+    _raise("kv_dequant_slots", load_library().kv_dequant_slots(layout, _ptr(pool), num_pages,
+                                                               _ptr(slots), n, _ptr(out), _stream(stream)))
     return out
 
 

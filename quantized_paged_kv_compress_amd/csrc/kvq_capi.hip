@@ -219,6 +219,21 @@ int kv_dequant(int32_t layout, const void* pool, int64_t num_pages, const int32_
     return launch(kvq::dequant_kernel<Layout::V41_FP4, 1>, grid, block, stream, p, num_pages, page_ids, P, out);
 }
 
+int kv_dequant_slots(int32_t layout, const void* pool, int64_t num_pages, const int32_t* slots, int64_t n,
+                     uint16_t* out, void* stream) {
+    if (!known_layout(layout)) return KVQ_ELAYOUT;
+    if (n < 0 || n > kMaxRows || num_pages < 0) return KVQ_EINVAL;
+    if (n == 0) return KVQ_OK;
+    if (!pool || !slots || !out) return KVQ_EINVAL;
+    if (!aligned16(pool) || !aligned16(out)) return KVQ_EINVAL;
+    const dim3 grid(blocks_for(n, kvq::kRowsPerBlock)), block(kvq::kWave * kvq::kRowsPerBlock);
+    const auto* p = static_cast<const uint8_t*>(pool);
+    const int64_t nslots = num_pages << kvq::kPageBits;
+    if (layout == KVQ_LAYOUT_V41)
+        return launch(kvq::dequant_slots_kernel<Layout::V41>, grid, block, stream, p, nslots, slots, n, out);
+    return launch(kvq::dequant_slots_kernel<Layout::V41_FP4>, grid, block, stream, p, nslots, slots, n, out);
+}
+
 int kv_translate_slots(const int32_t* table, int64_t table_len, const int32_t* full_loc, int64_t n,
                        int32_t* out, int64_t cap, void* stream) {
     if (n < 0 || cap < 0 || table_len < 0 || cap > kMaxRows) return KVQ_EINVAL;

@@ -224,16 +224,69 @@ __global__ __launch_bounds__(kWave * kWaves) void compress_long_kernel(
 }
 
 // ------------------------------------------------------------------ dequant
-// Each wavefront dequantises kRowsPerWave consecutive rows of one listed page: lane l
-// reads its 8 codes and the scale byte of its block for every row (all loads issued
-// before any use), then writes 8 bf16 (16 B) per row.  One row per wavefront suits
-// short page lists (more wavefronts to spread the launch); longer lists use 4 rows per
-// wavefront to keep more bytes in flight per wavefront.
+// Lane l's share of one stored row: its 8 codes (channels 8l..8l+7; one 8-byte V41 load
+// or one 4-byte FP4 load) and the scale byte of its block.
+template <Layout L>
+__device__ __forceinline__ void load_stored_row(const uint8_t* __restrict__ pg, int row, int lane,
+                                                uint32_t (&cw)[2], uint32_t& sb) {
+    using T = LayoutTraits<L>;
+    const uint8_t* code_row = pg + row * T::kCodeRowBytes;
+    if constexpr (L == Layout::V41) {
+        const uint2 c = *reinterpret_cast<const uint2*>(code_row + kElemsPerLane * lane);
+        cw[0] = c.x;
+        cw[1] = c.y;
+    } else {
+        cw[0] = *reinterpret_cast<const uint32_t*>(code_row + T::kCodeBytesPerLane * lane);
+        cw[1] = 0;
+    }
+    sb = pg[(int64_t(1) << kPageBits) * T::kCodeRowBytes + row * T::kScaleRowBytes + (lane >> 2)];
+}
+
+// decode(code) * decode(scale) in fp32, rounded to bf16; NaN codes or scales give 0x7FC0.
+// Writes the lane's 8 bf16 values (16 bytes) at dst.
+template <Layout L>
+__device__ __forceinline__ void dequant_lane(const uint32_t (&cw)[2], uint32_t sb, uint16_t* __restrict__ dst,
+                                             int lane) {
+    uint32_t o[8];
+    if constexpr (L == Layout::V41) {
+        const int k = static_cast<int>(sb) - 127;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t c = (cw[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+            const uint32_t mag = c & 0x7Fu;
+            const float val = __builtin_amdgcn_ldexpf(e4m3_mag_value(mag), k);  // exact unless it
+            uint32_t b = bf16_rne_bits(val) | ((c & 0x80u) << 8);               // under/overflows
+            if (mag == 0x7Fu || sb == 0xFFu) b = 0x7FC0u;
+            o[e] = b;
+        }
+    } else {
+        const bool nan_scale = (sb & 0x7Fu) == 0x7Fu;
+        const float s = (sb & 0x80u) ? -e4m3_mag_value(sb & 0x7Fu) : e4m3_mag_value(sb & 0x7Fu);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t nib = (cw[0] >> (4 * e)) & 0xFu;
+            const uint32_t ex = (nib >> 1) & 3u, mb = nib & 1u;
+            const float mag = ex ? __uint_as_float(((ex + 126u) << 23) | (mb << 22)) : 0.5f * static_cast<float>(mb);
+            const float val = ((nib & 8u) ? -mag : mag) * s;  // exact: at most 5 significant bits
+            o[e] = nan_scale ? 0x7FC0u : bf16_rne_bits(val);
+        }
+    }
+    uint4 st;
+    st.x = o[0] | (o[1] << 16);
+    st.y = o[2] | (o[3] << 16);
+    st.z = o[4] | (o[5] << 16);
+    st.w = o[6] | (o[7] << 16);
+    *reinterpret_cast<uint4*>(dst + kElemsPerLane * lane) = st;
+}
+
+// Whole pages: each wavefront dequantises kRowsPerWave consecutive rows of one listed
+// page (all loads issued before any use).  One row per wavefront suits short page lists
+// (more wavefronts to spread the launch); longer lists use 4 rows per wavefront to keep
+// more bytes in flight per wavefront.
 template <Layout L, int kRowsPerWave>
 __global__ __launch_bounds__(kWave * kRowsPerBlock) void dequant_kernel(
     const uint8_t* __restrict__ pool, int64_t num_pages, const int32_t* __restrict__ page_ids,
     int64_t P, uint16_t* __restrict__ out) {
-    using T = LayoutTraits<L>;
     static_assert((1 << kPageBits) % kRowsPerWave == 0, "a wavefront stays inside one page");
     constexpr int64_t kPB = kv_page_bytes<L>(1 << kPageBits);
     const int lane = threadIdx.x & (kWave - 1);
@@ -243,54 +296,29 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void dequant_kernel(
     if (page < 0 || page >= num_pages) return;
     const int row0 = static_cast<int>(g0 & ((1 << kPageBits) - 1));
     const uint8_t* pg = pool + static_cast<int64_t>(page) * kPB;
-
     uint32_t cw[kRowsPerWave][2], sb[kRowsPerWave];
 #pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) {
-        const uint8_t* code_row = pg + (row0 + r) * T::kCodeRowBytes;
-        if constexpr (L == Layout::V41) {
-            const uint2 c = *reinterpret_cast<const uint2*>(code_row + kElemsPerLane * lane);
-            cw[r][0] = c.x;
-            cw[r][1] = c.y;
-        } else {
-            cw[r][0] = *reinterpret_cast<const uint32_t*>(code_row + T::kCodeBytesPerLane * lane);
-            cw[r][1] = 0;
-        }
-        sb[r] = pg[(int64_t(1) << kPageBits) * T::kCodeRowBytes + (row0 + r) * T::kScaleRowBytes + (lane >> 2)];
-    }
+    for (int r = 0; r < kRowsPerWave; ++r) load_stored_row<L>(pg, row0 + r, lane, cw[r], sb[r]);
 #pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) {
-        uint32_t o[8];
-        if constexpr (L == Layout::V41) {
-            const int k = static_cast<int>(sb[r]) - 127;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t c = (cw[r][e >> 2] >> (8 * (e & 3))) & 0xFFu;
-                const uint32_t mag = c & 0x7Fu;
-                const float val = __builtin_amdgcn_ldexpf(e4m3_mag_value(mag), k);  // exact unless it
-                uint32_t b = bf16_rne_bits(val) | ((c & 0x80u) << 8);               // under/overflows
-                if (mag == 0x7Fu || sb[r] == 0xFFu) b = 0x7FC0u;
-                o[e] = b;
-            }
-        } else {
-            const bool nan_scale = (sb[r] & 0x7Fu) == 0x7Fu;
-            const float s = (sb[r] & 0x80u) ? -e4m3_mag_value(sb[r] & 0x7Fu) : e4m3_mag_value(sb[r] & 0x7Fu);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t nib = (cw[r][0] >> (4 * e)) & 0xFu;
-                const uint32_t ex = (nib >> 1) & 3u, mb = nib & 1u;
-                const float mag = ex ? __uint_as_float(((ex + 126u) << 23) | (mb << 22)) : 0.5f * static_cast<float>(mb);
-                const float val = ((nib & 8u) ? -mag : mag) * s;  // exact: at most 5 significant bits
-                o[e] = nan_scale ? 0x7FC0u : bf16_rne_bits(val);
-            }
-        }
-        uint4 st;
-        st.x = o[0] | (o[1] << 16);
-        st.y = o[2] | (o[3] << 16);
-        st.z = o[4] | (o[5] << 16);
-        st.w = o[6] | (o[7] << 16);
-        *reinterpret_cast<uint4*>(out + (g0 + r) * kHeadDim + kElemsPerLane * lane) = st;
-    }
+    for (int r = 0; r < kRowsPerWave; ++r) dequant_lane<L>(cw[r], sb[r], out + (g0 + r) * kHeadDim, lane);
+}
+
+// Token gather: output row g is the dequantised row at slots[g]; rows whose slot is
+// outside the pool are left untouched.
+template <Layout L>
+__global__ __launch_bounds__(kWave * kRowsPerBlock) void dequant_slots_kernel(
+    const uint8_t* __restrict__ pool, int64_t nslots, const int32_t* __restrict__ slots, int64_t n,
+    uint16_t* __restrict__ out) {
+    constexpr int64_t kPB = kv_page_bytes<L>(1 << kPageBits);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t g = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave_id();
+    if (g >= n) return;
+    const int32_t slot = slots[g];
+    if (slot < 0 || slot >= nslots) return;
+    const uint8_t* pg = pool + static_cast<int64_t>(slot >> kPageBits) * kPB;
+    uint32_t cw[2], sb;
+    load_stored_row<L>(pg, slot & ((1 << kPageBits) - 1), lane, cw, sb);
+    dequant_lane<L>(cw, sb, out + g * kHeadDim, lane);
 }
 
 // ------------------------------------------------------------------ full -> SWA slots

@@ -147,6 +147,11 @@ def test_dequant_and_translate_argument_checks(kvq):
     assert L.kv_dequant(V41, A, 4, B, 1, None, None) == kvq.KVQ_EINVAL
     assert L.kv_dequant(FP4, A, 4, B, 1, C + 2, None) == kvq.KVQ_EINVAL
     assert L.kv_dequant(FP4, A, 4, B, -1, C, None) == kvq.KVQ_EINVAL
+    assert L.kv_dequant_slots(5, A, 4, B, 1, C, None) == kvq.KVQ_ELAYOUT
+    assert L.kv_dequant_slots(V41, A, 4, B, 0, C, None) == kvq.KVQ_OK
+    assert L.kv_dequant_slots(V41, A, 4, None, 1, C, None) == kvq.KVQ_EINVAL
+    assert L.kv_dequant_slots(V41, A, 4, B, 1, C + 4, None) == kvq.KVQ_EINVAL
+    assert L.kv_dequant_slots(FP4, A, 4, B, -2, C, None) == kvq.KVQ_EINVAL
     # translate: n > cap is refused before anything else happens
     assert L.kv_translate_slots(A, 100, B, 11, C, 10, None) == kvq.KVQ_ECAPACITY
     assert L.kv_translate_slots(None, 0, None, 11, None, 10, None) == kvq.KVQ_ECAPACITY

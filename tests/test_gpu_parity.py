@@ -386,6 +386,23 @@ def test_dequant_long_page_list_bit_exact(kvq, orc, layout):
     assert np.array_equal(to_host(out), ref)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("n", [1, 77, 2049])
+def test_dequant_slots_bit_exact(kvq, orc, layout, n):
+    import torch
+    rng = np.random.default_rng(17 + n)
+    num_pages = 40
+    pool = rng.integers(0, 256, (num_pages, kvq.page_bytes(layout))).astype(np.uint8)
+    slots = rng.integers(0, num_pages * 64, n).astype(np.int32)
+    if n > 3:
+        slots[[0, 1, 2]] = [-5, num_pages * 64, 3]
+    out = torch.full((n, 512), 0x3579, dtype=torch.int16, device="cuda")
+    kvq.kv_dequant_slots(to_dev(pool), layout, to_dev(slots), out)
+    ref = np.full((n, 512), 0x3579, np.uint16)
+    orc.kv_dequant_slots(layout, pool, slots, ref)
+    assert np.array_equal(to_host(out), ref)
+
+
 # ------------------------------------------------------------------ translate
 def test_translate_semantics(kvq, orc):
     import torch

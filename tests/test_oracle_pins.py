@@ -816,3 +816,23 @@ def test_norm_rope_store_composes(orc):
         orc.kv_store_norm_rope(layout, a, k, w, 1e-6, pos, cs, slots)
         orc.kv_store_rope(layout, b, normed, pos, cs, slots)
         assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- token-gather dequant
+@pytest.mark.parametrize("layout", [V41, FP4])
+def test_dequant_slots_matches_page_dequant(orc, layout):
+    """Row i of the token gather equals row (slot & 63) of page (slot >> 6) of the page
+    dequant (pinned exhaustively above); out-of-pool slots leave their rows untouched."""
+    rng = np.random.default_rng(54)
+    num_pages = 6
+    pool = rng.integers(0, 256, (num_pages, orc.page_bytes(layout))).astype(np.uint8)
+    pages = orc.kv_dequant(layout, pool, np.arange(num_pages, dtype=np.int32))
+    slots = rng.integers(0, num_pages * 64, 300).astype(np.int32)
+    slots[[5, 6, 7]] = [-1, num_pages * 64, 2 ** 31 - 1]
+    out = np.full((300, 512), 0x1234, np.uint16)
+    orc.kv_dequant_slots(layout, pool, slots, out)
+    for i, sl in enumerate(slots):
+        if 0 <= sl < num_pages * 64:
+            assert np.array_equal(out[i], pages[sl])
+        else:
+            assert np.all(out[i] == 0x1234)
