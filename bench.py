@@ -170,6 +170,52 @@ def micro_bench(kvq, wl, dev, cs, layers=61, reps=20, calls=50):
             "latency_us": table, "swa_hoisting": step}
 
 
+def ratio_sweep(kvq, wl, dev, cs, kv, sc, c4_pool, c4_slots, reps=5):
+    """NEXT-row measurements on the resident C128A inputs (2,097,152 fp32 rows of kv and
+    score): every supported ratio r >= 2 compresses the same input rows into 2,097,152 / r
+    output rows (V41); and the token-gather dequant of the 16,384 C4A rows."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(77)
+    rows_in = kv.shape[0]
+    pool = kvq.new_pool(kvq.V41, 8192)
+    sweep = {}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for r in (2, 4, 8, 16, 32, 64, 128):
+        R = rows_in // r
+        pos = torch.from_numpy(rng.integers(0, 65536, R).astype(np.int32)).to(dev)
+        slots = torch.from_numpy(wl.distinct_slots(rng, R, 64, 8192 * 64)).to(dev)
+        times = []
+        for k in range(reps + 1):
+            ev[0].record()
+            kvq.kv_compress_store(pool, kvq.V41, kv[:R * r], sc[:R * r], r, pos, cs, slots)
+            ev[1].record()
+            ev[1].synchronize()
+            if k:
+                times.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        us = float(np.median(times))
+        b = bytes_compress(R, r, kvq.bytes_per_token(kvq.V41))
+        sweep[f"r{r}"] = {"rows": R, "us": round(us, 1), "GB/s": round(b / us / 1e3, 1),
+                          "frac_of_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+    out = torch.empty((c4_slots.numel(), HEAD), dtype=torch.bfloat16, device=dev)
+    times = []
+    for k in range(reps + 1):
+        ev[0].record()
+        kvq.kv_dequant_slots(c4_pool, kvq.V41, c4_slots, out)
+        ev[1].record()
+        ev[1].synchronize()
+        if k:
+            times.append(ev[0].elapsed_time(ev[1]) * 1e3)
+    us = float(np.median(times))
+    n = c4_slots.numel()
+    b = n * (4 + kvq.bytes_per_token(kvq.V41) + HEAD * 2)
+    gather = {"rows": n, "us": round(us, 2), "GB/s": round(b / us / 1e3, 1),
+              "frac_of_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return {"method": "HIP events, median of %d launches; the ratio sweep reads the same 8 GiB "
+                      "of cold inputs at every ratio" % reps,
+            "compress_ratio_sweep_v41": sweep, "dequant_slots_c4a_rows": gather}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,10 +363,12 @@ def main():
     dom = "compress_c128a"
     traffic = read_traffic(alg[dom])
 
-    micro = None
+    micro = nxt = None
     if not args.no_micro:
         micro = micro_bench(kvq, wl, dev, cs)
         log(f"micro: {micro['latency_us']}; hoisting {micro['swa_hoisting']}")
+        nxt = ratio_sweep(kvq, wl, dev, cs, c128["kv"], c128["sc"], c4["pool"], c4["slots"])
+        log(f"ratio sweep: {nxt['compress_ratio_sweep_v41']}; gather {nxt['dequant_slots_c4a_rows']}")
 
     # ------------------------------------------------------------ CPU oracle baseline
     cpu = None
@@ -376,6 +424,7 @@ def main():
         "kernels": kernels,
         "copy_1GiB_GB/s": round(copy_gbs, 1),
         "micro": micro,
+        "next_rows": nxt,
         "c4a": {"rows/s": kernels["compress_c4a"]["rows/s"], "GB/s": kernels["compress_c4a"]["GB/s"],
                 "frac_of_peak": kernels["compress_c4a"]["frac_of_peak"]},
         "c128a": {"rows/s": kernels[dom]["rows/s"], "GB/s": kernels[dom]["GB/s"],
