@@ -178,13 +178,14 @@ def ratio_sweep(kvq, wl, dev, cs, kv, sc, c4_pool, c4_slots, reps=5):
     import torch
     rng = np.random.default_rng(77)
     rows_in = kv.shape[0]
-    pool = kvq.new_pool(kvq.V41, 8192)
+    num_pages = 20000          # room for 1,048,576 distinct slots (ratio 2)
+    pool = kvq.new_pool(kvq.V41, num_pages)
     sweep = {}
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     for r in (2, 4, 8, 16, 32, 64, 128):
         R = rows_in // r
         pos = torch.from_numpy(rng.integers(0, 65536, R).astype(np.int32)).to(dev)
-        slots = torch.from_numpy(wl.distinct_slots(rng, R, 64, 8192 * 64)).to(dev)
+        slots = torch.from_numpy(wl.distinct_slots(rng, R, 64, num_pages * 64)).to(dev)
         times = []
         for k in range(reps + 1):
             ev[0].record()
