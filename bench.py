@@ -212,9 +212,36 @@ def ratio_sweep(kvq, wl, dev, cs, kv, sc, c4_pool, c4_slots, reps=5):
     b = n * (4 + kvq.bytes_per_token(kvq.V41) + HEAD * 2)
     gather = {"rows": n, "us": round(us, 2), "GB/s": round(b / us / 1e3, 1),
               "frac_of_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+    # decode steps with the compressor state: 16,384 sequences add one row per call; one
+    # full window (ratio calls) is timed, V41
+    S = 16384
+    state_pool = kvq.new_pool(kvq.V41, 4096)
+    decode = {}
+    for r in (4, 128):
+        state, count = kvq.new_compress_state(S)
+        ids = torch.randperm(S, device=dev, dtype=torch.int64).to(torch.int32)
+        pos = torch.from_numpy(rng.integers(0, 65536, S).astype(np.int32)).to(dev)
+        slots = torch.from_numpy(wl.distinct_slots(rng, S, 64, 4096 * 64)).to(dev)
+        step_rows = [(kv[(k % 64) * S:(k % 64 + 1) * S], sc[(k % 64) * S:(k % 64 + 1) * S]) for k in range(r)]
+        for k in range(r):      # one untimed window
+            kvq.kv_compress_state_update(state_pool, kvq.V41, state, count, r, ids, step_rows[k][0],
+                                         step_rows[k][1], pos, cs, slots)
+        ev[0].record()
+        for k in range(r):
+            kvq.kv_compress_state_update(state_pool, kvq.V41, state, count, r, ids, step_rows[k][0],
+                                         step_rows[k][1], pos, cs, slots)
+        ev[1].record()
+        ev[1].synchronize()
+        us = ev[0].elapsed_time(ev[1]) * 1e3
+        b = S * (r * (HEAD * 8 + 4 + 8) + 2 * (r - 1) * 3 * HEAD * 4 + 4 + 4 + 256 +
+                 kvq.bytes_per_token(kvq.V41))
+        decode[f"r{r}"] = {"sequences": S, "us_per_step": round(us / r, 2), "GB/s": round(b / us / 1e3, 1),
+                           "frac_of_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
     return {"method": "HIP events, median of %d launches; the ratio sweep reads the same 8 GiB "
-                      "of cold inputs at every ratio" % reps,
-            "compress_ratio_sweep_v41": sweep, "dequant_slots_c4a_rows": gather}
+                      "of cold inputs at every ratio; decode steps fold one row per sequence into "
+                      "its 6 KiB state per call (one full window timed)" % reps,
+            "compress_ratio_sweep_v41": sweep, "dequant_slots_c4a_rows": gather,
+            "compress_state_decode_v41": decode}
 
 
 def main():

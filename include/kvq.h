@@ -138,6 +138,30 @@ int kv_compress_store(int32_t layout, void* pool, int64_t num_pages, const float
                       const float* cos_sin, int64_t max_pos, const int32_t* slots,
                       int64_t R, void* stream);
 
+/* kv_compress_state_update -- the compressor across decode steps: windows that fill one
+ * row per step are folded into a per-sequence online-softmax state instead of keeping
+ * their raw rows (the decode side of the mixed decode/prefill batches of [P3]'s
+ * introduction).  For each j < n, row j (kv[j], score[j]) is folded into state
+ * state_ids[j] and counted; when the count reaches `ratio` the window is finalised
+ * exactly as kv_compress_store finalises a window (pooled value rounded to bf16, RoPE at
+ * pos[j], quantise, store at slots[j]; an out-of-pool slot or out-of-range position
+ * stores nothing) and the state becomes empty again.  Rows of one window must arrive in
+ * order, at most one row per state per call (state_ids distinct within a call; repeats
+ * race).  A state id outside [0, num_states) skips the row.
+ *   state      device fp32 [num_states][3][512], contents opaque; 16-byte aligned
+ *   count      device int32 [num_states]: rows folded so far; 0 = empty.  A zeroed
+ *              state + count is a valid starting point.
+ *   ratio      window length, 1 .. 2^20
+ *   pos, slots device int32[n]: used for the row that completes its window
+ *   kv, score  device fp32 rows, row j at base + j*ld; 16-byte aligned, ld >= 512, % 4
+ * The finalised row may differ from kv_compress_store on the same window by at most one
+ * code step (the fold runs in a different fp32 order). */
+int kv_compress_state_update(int32_t layout, void* pool, int64_t num_pages, float* state,
+                             int32_t* count, int64_t num_states, int32_t ratio,
+                             const int32_t* state_ids, const float* kv, const float* score,
+                             int64_t ld, const int32_t* pos, const float* cos_sin,
+                             int64_t max_pos, const int32_t* slots, int64_t n, void* stream);
+
 /* kv_dequant -- turn whole pages back into a bf16 workspace ([P1] section 4).
  * For p < P and each of the 64 rows r of page page_ids[p]:
  *   out[(p*64 + r)*512 + c] = bf16_rne(fp32(decode(code) * decode(scale)))

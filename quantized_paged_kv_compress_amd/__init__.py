@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "V41", "V41_FP4", "KVQError", "load_library", "bytes_per_token", "page_bytes",
     "code_row_bytes", "scale_row_bytes", "new_pool", "kv_store", "kv_store_rope", "kv_store_norm_rope",
-    "kv_compress_store", "kv_dequant", "kv_dequant_slots", "kv_translate_slots", "SUPPORTED_RATIOS",
+    "kv_compress_store", "kv_compress_state_update", "new_compress_state", "kv_dequant", "kv_dequant_slots", "kv_translate_slots", "SUPPORTED_RATIOS",
 ]
 
 V41 = 1
@@ -58,6 +58,8 @@ def load_library() -> ctypes.CDLL:
         "kv_store_rope": [i32, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp],
         "kv_store_norm_rope": [i32, vp, i64, vp, i64, vp, ctypes.c_float, vp, vp, i64, vp, i64, vp],
         "kv_compress_store": [i32, vp, i64, vp, vp, i64, i32, vp, vp, i64, vp, i64, vp],
+        "kv_compress_state_update": [i32, vp, i64, vp, vp, i64, i32, vp, vp, vp, i64, vp, vp, i64, vp,
+                                     i64, vp],
         "kv_dequant": [i32, vp, i64, vp, i64, vp, vp],
         "kv_dequant_slots": [i32, vp, i64, vp, i64, vp, vp],
         "kv_translate_slots": [vp, i64, vp, i64, vp, i64, vp],
@@ -208,6 +210,40 @@ def kv_compress_store(pool, layout, kv, score, ratio, pos, cos_sin, slots, strea
     _raise("kv_compress_store", load_library().kv_compress_store(
         layout, _ptr(pool), num_pages, _ptr(kv), _ptr(score), ld, ratio, _ptr(pos),
         _ptr(cos_sin), cos_sin.shape[0], _ptr(slots), R, _stream(stream)))
+
+
+def new_compress_state(num_states: int, device="cuda"):
+    """An empty decode-step compressor state: (fp32 [num_states, 3, 512], int32 counts)."""
+    return (torch.zeros((num_states, 3, HEAD_DIM), dtype=torch.float32, device=device),
+            torch.zeros(num_states, dtype=torch.int32, device=device))
+
+
+def kv_compress_state_update(pool, layout, state, count, ratio, state_ids, kv, score, pos,
+                             cos_sin, slots, stream=None):
+    """Fold row j of kv/score into state state_ids[j]; a window completed by row j is
+    stored at slots[j] with RoPE at pos[j].  At most one row per state per call."""
+    num_pages = _pool(pool, layout)
+    _dev(state, "state", _F32)
+    _dev(count, "count", _I32)
+    if not state.is_contiguous() or state.dim() != 3 or tuple(state.shape[1:]) != (3, HEAD_DIM):
+        raise ValueError("state: need a contiguous fp32 [num_states, 3, 512] tensor")
+    if count.numel() != state.shape[0]:
+        raise ValueError("count: one int32 per state")
+    ld = _rows(_dev(kv, "kv", _F32), "kv")
+    if _rows(_dev(score, "score", _F32), "score") != ld or score.shape[0] != kv.shape[0]:
+        raise ValueError("score must match kv in shape and stride")
+    for t, nm in ((state_ids, "state_ids"), (pos, "pos"), (slots, "slots")):
+        _dev(t, nm, _I32)
+    _dev(cos_sin, "cos_sin", _F32)
+    if not cos_sin.is_contiguous() or cos_sin.dim() != 2 or cos_sin.shape[1] != ROPE_DIM:
+        raise ValueError("cos_sin: need a contiguous fp32 [max_pos, 64] tensor")
+    n = state_ids.numel()
+    if kv.shape[0] < n or pos.numel() != n or slots.numel() != n:
+        raise ValueError("kv / state_ids / pos / slots sizes disagree")
+    _raise("kv_compress_state_update", load_library().kv_compress_state_update(
+        layout, _ptr(pool), num_pages, _ptr(state), _ptr(count), state.shape[0], ratio,
+        _ptr(state_ids), _ptr(kv), _ptr(score), ld, _ptr(pos), _ptr(cos_sin), cos_sin.shape[0],
+        _ptr(slots), n, _stream(stream)))
 
 
 def kv_dequant(pool, layout, page_ids, out=None, stream=None):

@@ -19,6 +19,7 @@ using kvq::Layout;
 
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 constexpr int64_t kDequantLongList = 1024;  // pages; from here on 4 rows per wavefront
+constexpr int32_t kMaxStateRatio = 1 << 20;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -195,6 +196,29 @@ int kv_compress_store(int32_t layout, void* pool, int64_t num_pages, const float
     if (layout == KVQ_LAYOUT_V41)
         return compress_dispatch<Layout::V41>(ratio, pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
     return compress_dispatch<Layout::V41_FP4>(ratio, pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
+}
+
+int kv_compress_state_update(int32_t layout, void* pool, int64_t num_pages, float* state, int32_t* count,
+                             int64_t num_states, int32_t ratio, const int32_t* state_ids, const float* kv,
+                             const float* score, int64_t ld, const int32_t* pos, const float* cos_sin,
+                             int64_t max_pos, const int32_t* slots, int64_t n, void* stream) {
+    if (!known_layout(layout)) return KVQ_ELAYOUT;
+    if (ratio < 1 || ratio > kMaxStateRatio) return KVQ_ERATIO;
+    if (n < 0 || n > kMaxRows || num_pages < 0 || num_states < 0 || max_pos <= 0) return KVQ_EINVAL;
+    if (n == 0) return KVQ_OK;
+    if (!pool || !state || !count || !state_ids || !kv || !score || !pos || !cos_sin || !slots)
+        return KVQ_EINVAL;
+    if (ld < kvq::kHeadDim || ld % 4 != 0) return KVQ_EINVAL;
+    if (!aligned16(pool) || !aligned16(state) || !aligned16(kv) || !aligned16(score) || !aligned16(cos_sin))
+        return KVQ_EINVAL;
+    const dim3 grid(blocks_for(n, kvq::kRowsPerBlock)), block(kvq::kWave * kvq::kRowsPerBlock);
+    auto* p = static_cast<uint8_t*>(pool);
+    const int64_t nslots = num_pages << kvq::kPageBits;
+    if (layout == KVQ_LAYOUT_V41)
+        return launch(kvq::compress_state_kernel<Layout::V41>, grid, block, stream, p, nslots, state, count,
+                      num_states, ratio, state_ids, kv, score, ld, pos, cos_sin, max_pos, slots, n);
+    return launch(kvq::compress_state_kernel<Layout::V41_FP4>, grid, block, stream, p, nslots, state, count,
+                  num_states, ratio, state_ids, kv, score, ld, pos, cos_sin, max_pos, slots, n);
 }
 
 int kv_dequant(int32_t layout, const void* pool, int64_t num_pages, const int32_t* page_ids,

@@ -223,6 +223,72 @@ __global__ __launch_bounds__(kWave * kWaves) void compress_long_kernel(
     quantize_store_row<L>(pool, static_cast<uint32_t>(slot), v, lane);
 }
 
+// ------------------------------------------------------------------ decode-step compressor state
+// One row per state (sequence) per call: fold the row into the state's online softmax
+// (m in log2 units, l, acc per channel; 3 x 512 fp32 in channel order), count it, and
+// when the window is complete, finalise like the window kernels (acc / l rounded to bf16,
+// RoPE at the completing row's position, quantise, store at its slot) and reset the
+// count.  count == 0 means an empty state, so a zeroed buffer is a valid start.
+template <Layout L>
+__global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_state_kernel(
+    uint8_t* __restrict__ pool, int64_t nslots, float* __restrict__ state, int32_t* __restrict__ count,
+    int64_t num_states, int32_t ratio, const int32_t* __restrict__ state_ids, const float* __restrict__ kv,
+    const float* __restrict__ score, int64_t ld, const int32_t* __restrict__ pos,
+    const float* __restrict__ cos_sin, int64_t max_pos, const int32_t* __restrict__ slots, int64_t n) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t j = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave_id();
+    if (j >= n) return;
+    const int32_t sid = state_ids[j];
+    if (sid < 0 || sid >= num_states) return;
+    float x[8], s[8];
+    load_row_f32(kv + j * ld, lane, x);
+    load_row_f32(score + j * ld, lane, s);
+    float* st = state + static_cast<int64_t>(sid) * 3 * kHeadDim;
+    const int32_t c = count[sid];
+    float m[8], l[8], acc[8];
+    if (c == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { m[e] = s[e] * kLog2e; l[e] = 1.0f; acc[e] = x[e]; }
+    } else {
+        float pm[8], pl[8], pa[8];
+        load_row_f32(st, lane, pm);
+        load_row_f32(st + kHeadDim, lane, pl);
+        load_row_f32(st + 2 * kHeadDim, lane, pa);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float mn = fmaxf(pm[e], s[e] * kLog2e);
+            const float alpha = __builtin_amdgcn_exp2f(pm[e] - mn);
+            const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], kLog2e, -mn));
+            m[e] = mn;
+            l[e] = __builtin_fmaf(pl[e], alpha, w);
+            acc[e] = __builtin_fmaf(pa[e], alpha, w * x[e]);
+        }
+    }
+    if (c + 1 < ratio) {
+        float* dst[3] = {st, st + kHeadDim, st + 2 * kHeadDim};
+        const float* src[3] = {m, l, acc};
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            *reinterpret_cast<float4*>(dst[q] + 4 * lane) = make_float4(src[q][0], src[q][1], src[q][2], src[q][3]);
+            *reinterpret_cast<float4*>(dst[q] + kHalf + 4 * lane) = make_float4(src[q][4], src[q][5], src[q][6], src[q][7]);
+        }
+        if (lane == 0) count[sid] = c + 1;
+        return;
+    }
+    if (lane == 0) count[sid] = 0;  // the window is complete: the state is consumed
+    const int32_t p = pos[j];
+    const int32_t slot = slots[j];
+    const bool valid = slot >= 0 && slot < nslots && p >= 0 && p < max_pos;
+    RopeCS cs;
+    rope_load_cs(cos_sin + static_cast<int64_t>(valid ? p : 0) * kRopeDim, lane, cs);
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = round_bf16(acc[e] * __builtin_amdgcn_rcpf(l[e]));
+    rope_apply(v, cs, lane);
+    if (!valid) return;
+    quantize_store_row<L>(pool, static_cast<uint32_t>(slot), v, lane);
+}
+
 // ------------------------------------------------------------------ dequant
 // Lane l's share of one stored row: its 8 codes (channels 8l..8l+7; one 8-byte V41 load
 // or one 4-byte FP4 load) and the scale byte of its block.

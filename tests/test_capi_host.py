@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for want in ("kv_store", "kv_store_rope", "kv_store_norm_rope", "kv_compress_store", "kv_dequant",
+    for want in ("kv_store", "kv_store_rope", "kv_store_norm_rope", "kv_compress_store",
+                 "kv_compress_state_update", "kv_dequant_slots", "kv_dequant",
                  "kv_translate_slots", "kvq_bytes_per_token", "kvq_page_bytes"):
         assert want in names
 
@@ -110,6 +111,26 @@ def test_store_norm_rope_argument_checks(kvq):
     assert call(max_pos=0) == kvq.KVQ_EINVAL
     assert call(pos=None) == kvq.KVQ_EINVAL
     assert call(layout=3) == kvq.KVQ_ELAYOUT
+
+
+def test_compress_state_argument_checks(kvq):
+    L = kvq.load_library()
+    ok = dict(layout=V41, pool=A, num_pages=4, state=B, count=C, num_states=8, ratio=4, ids=A, kv=B,
+              score=C, ld=512, pos=A, cs=B, max_pos=10, slots=C, n=3, stream=None)
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.kv_compress_state_update(*a.values())
+    assert call(n=0) == kvq.KVQ_OK
+    assert call(layout=9) == kvq.KVQ_ELAYOUT
+    assert call(ratio=0) == kvq.KVQ_ERATIO
+    assert call(ratio=(1 << 20) + 1) == kvq.KVQ_ERATIO
+    for k in ("pool", "state", "count", "ids", "kv", "score", "pos", "cs", "slots"):
+        assert call(**{k: None}) == kvq.KVQ_EINVAL, k
+    assert call(state=B + 4) == kvq.KVQ_EINVAL
+    assert call(ld=500) == kvq.KVQ_EINVAL
+    assert call(num_states=-1) == kvq.KVQ_EINVAL
+    assert call(max_pos=0) == kvq.KVQ_EINVAL
 
 
 def test_compress_argument_checks(kvq):

@@ -326,6 +326,63 @@ def test_c128a_full_size_sampled(kvq, orc, cos_sin, cos_sin_dev):
     sampled_compressor_check(kvq, orc, V41, 128, 16384, 4, 96, cos_sin, cos_sin_dev)
 
 
+# ------------------------------------------------------------------ decode-step state
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("ratio,S,T", [(1, 40, 5), (4, 96, 41), (128, 24, 300)])
+def test_compress_state_decode_steps(kvq, orc, cos_sin, cos_sin_dev, layout, ratio, S, T):
+    """S sequences add one row per step (sequence s joins at step t0[s]); every completed
+    window must equal the batch compressor's result on the same rows (tolerance rule),
+    incomplete windows store nothing, and the counts end at (rows seen) mod ratio."""
+    import torch
+    rng = np.random.default_rng(1000 * ratio + S)
+    num_pages = 64
+    t0 = rng.integers(0, max(1, T // 3), S)
+    nrows = np.maximum(T - t0, 0)
+    nwin = nrows // ratio
+    rows = [rng.standard_normal((nrows[s_], 512)).astype(np.float32) for s_ in range(S)]
+    scs = [(2 * rng.standard_normal((nrows[s_], 512))).astype(np.float32) for s_ in range(S)]
+    wslots = wl.distinct_slots(rng, int(nwin.sum()) + S, 64, num_pages * 64)
+    win_slot, win_pos, k_ = [], [], 0
+    for s_ in range(S):
+        win_slot.append(wslots[k_:k_ + nwin[s_] + 1]); k_ += nwin[s_] + 1
+        win_pos.append(rng.integers(0, 65536, nwin[s_] + 1).astype(np.int32))
+    pool = kvq.new_pool(layout, num_pages)
+    state, count = kvq.new_compress_state(S + 3)
+    sid_of = rng.permutation(S + 3)[:S].astype(np.int32)       # states need not be dense
+    for t in range(T):
+        act = [s_ for s_ in range(S) if t >= t0[s_]]
+        rng.shuffle(act)
+        if not act:
+            continue
+        r_idx = [t - t0[s_] for s_ in act]
+        kv = np.stack([rows[s_][r] for s_, r in zip(act, r_idx)])
+        sc = np.stack([scs[s_][r] for s_, r in zip(act, r_idx)])
+        w_idx = [r // ratio for r in r_idx]
+        pos = np.array([win_pos[s_][w] for s_, w in zip(act, w_idx)], np.int32)
+        slots = np.array([win_slot[s_][w] for s_, w in zip(act, w_idx)], np.int32)
+        kvq.kv_compress_state_update(pool, layout, state, count, ratio, to_dev(sid_of[act]), to_dev(kv),
+                                     to_dev(sc), to_dev(pos), cos_sin_dev, to_dev(slots))
+    torch.cuda.synchronize()
+    got = to_host(pool)
+    assert np.array_equal(to_host(count)[sid_of], (nrows % ratio).astype(np.int32))
+    ref = orc.new_pool(layout, num_pages)
+    done_slots, f64s = [], []
+    for s_ in range(S):
+        if nwin[s_] == 0:
+            continue
+        kvw = np.ascontiguousarray(rows[s_][:nwin[s_] * ratio])
+        scw = np.ascontiguousarray(scs[s_][:nwin[s_] * ratio])
+        sl = np.ascontiguousarray(win_slot[s_][:nwin[s_]])
+        orc.kv_compress_store(layout, ref, kvw, scw, ratio, np.ascontiguousarray(win_pos[s_][:nwin[s_]]),
+                              cos_sin, sl)
+        done_slots.append(sl)
+        f64s.append(orc.pool_rows(kvw, scw, ratio)[0])
+    done = np.concatenate(done_slots)
+    log(f"[state] ratio {ratio}: {done.size} windows completed over {T} steps")
+    compare_compressed(got, ref, layout, done, np.concatenate(f64s), label=f"state r{ratio} L{layout}")
+    assert untouched_equal(got, ref, layout, done)   # incomplete windows wrote nothing
+
+
 # ------------------------------------------------------------------ dequant
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_dequant_exhaustive_bit_exact(kvq, orc, layout):
