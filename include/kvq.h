@@ -32,7 +32,9 @@
  *    call are a caller error (which row wins is unspecified).
  *  - n == 0 (or R == 0, P == 0) returns KVQ_OK without launching, except
  *    kv_translate_slots, which still zeroes out[0:cap].
- *  - Inputs must be finite; non-finite values give unspecified codes.
+ *  - Inputs must be finite, with |kv| * ratio and |score| * 1.5 below FLT_MAX (the fp32
+ *    pooling sums at most `ratio` weighted rows and scales scores by log2(e));
+ *    values outside that domain give unspecified codes.  fp32 denormals are handled.
  *
  * Pool layout (PagedKV, page size 64 tokens, [P1] section 1): the pool is num_pages
  * pages of kvq_page_bytes(layout) bytes each, contiguous from `pool`.  Slot s lives in

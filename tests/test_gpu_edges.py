@@ -1,0 +1,150 @@
+"""Edge cases on the GPU: boundary slots and positions for every writing entry point, and
+compressor inputs at the edges of the domain (all-zero windows, fp32-denormal and very
+large kv, score spreads wide enough for exp to underflow), against the CPU oracle."""
+import numpy as np
+import pytest
+
+from helpers import FP4, V41, compare_compressed, gpu_lib, to_dev, to_host, untouched_equal
+from quantized_paged_kv_compress_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+LAYOUTS = [V41, FP4]
+NUM_PAGES = 6
+I32 = np.iinfo(np.int32)
+EDGE_SLOTS = np.array([0, 63, 64, NUM_PAGES * 64 - 1, NUM_PAGES * 64, -1, I32.max, I32.min,
+                       NUM_PAGES * 64 - 64, 1], np.int32)
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    return gpu_lib()
+
+
+@pytest.fixture(scope="module")
+def cs_small():
+    return wl.rope_cos_sin(max_pos=100)
+
+
+def canary(kvq, layout):
+    pool = kvq.new_pool(layout, NUM_PAGES)
+    pool.fill_(0x77)
+    return pool, np.full((NUM_PAGES, kvq.page_bytes(layout)), 0x77, np.uint8)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_boundary_slots_and_positions_store_paths(kvq, orc, cs_small, layout):
+    rng = np.random.default_rng(61)
+    n = EDGE_SLOTS.size
+    k = wl.bf16_bits(rng.standard_normal((n, 512)).astype(np.float32))
+    pos = np.array([0, 99, 50, 99, 3, 0, 1, 2, 100, -1], np.int32)   # 100 and -1 skip
+    w = wl.bf16_bits(rng.uniform(0.5, 1.5, 512).astype(np.float32))
+    for name in ("store", "rope", "norm"):
+        pool, ref = canary(kvq, layout)
+        if name == "store":
+            kvq.kv_store(pool, layout, to_dev(k), to_dev(EDGE_SLOTS))
+            orc.kv_store(layout, ref, k, EDGE_SLOTS)
+        elif name == "rope":
+            kvq.kv_store_rope(pool, layout, to_dev(k), to_dev(pos), to_dev(cs_small), to_dev(EDGE_SLOTS))
+            orc.kv_store_rope(layout, ref, k, pos, cs_small, EDGE_SLOTS)
+        else:
+            kvq.kv_store_norm_rope(pool, layout, to_dev(k), to_dev(w), 1e-6, to_dev(pos), to_dev(cs_small),
+                                   to_dev(EDGE_SLOTS))
+            orc.kv_store_norm_rope(layout, ref, k, w, 1e-6, pos, cs_small, EDGE_SLOTS)
+        got = to_host(pool)
+        if name == "norm":
+            valid = (EDGE_SLOTS >= 0) & (EDGE_SLOTS < NUM_PAGES * 64) & (pos >= 0) & (pos < 100)
+            compare_compressed(got, ref, layout, EDGE_SLOTS[valid], None, label=f"edge norm L{layout}")
+            assert untouched_equal(got, ref, layout, EDGE_SLOTS[valid])
+        else:
+            assert np.array_equal(got, ref), name
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("ratio", [1, 4, 128])
+def test_boundary_slots_compress(kvq, orc, cs_small, layout, ratio):
+    rng = np.random.default_rng(62 + ratio)
+    R = EDGE_SLOTS.size
+    kv = rng.standard_normal((R * ratio, 512)).astype(np.float32)
+    sc = (2 * rng.standard_normal((R * ratio, 512))).astype(np.float32)
+    pos = np.array([0, 99, 50, 99, 3, 0, 1, 2, 100, -1], np.int32)
+    pool, ref = canary(kvq, layout)
+    kvq.kv_compress_store(pool, layout, to_dev(kv), to_dev(sc) if ratio > 1 else None, ratio, to_dev(pos),
+                          to_dev(cs_small), to_dev(EDGE_SLOTS))
+    orc.kv_compress_store(layout, ref, kv, sc, ratio, pos, cs_small, EDGE_SLOTS)
+    got = to_host(pool)
+    valid = (EDGE_SLOTS >= 0) & (EDGE_SLOTS < NUM_PAGES * 64) & (pos >= 0) & (pos < 100)
+    f64, _ = orc.pool_rows(kv, sc, ratio)
+    compare_compressed(got, ref, layout, EDGE_SLOTS[valid], f64[valid], label=f"edge slots r{ratio}")
+    assert untouched_equal(got, ref, layout, EDGE_SLOTS[valid])
+
+
+def extreme_windows(rng, ratio, R):
+    """Window families: zeros, fp32-denormal kv, large kv, wide score spreads, ties."""
+    kv = rng.standard_normal((R * ratio, 512)).astype(np.float32)
+    sc = (2 * rng.standard_normal((R * ratio, 512))).astype(np.float32)
+    fam = np.arange(R) % 6
+    for i in range(R):
+        rows = slice(i * ratio, (i + 1) * ratio)
+        if fam[i] == 0:
+            kv[rows] = 0.0                                         # all-zero window
+        elif fam[i] == 1:
+            kv[rows] *= np.float32(1e-40)                          # fp32 denormals
+        elif fam[i] == 2:
+            kv[rows] *= np.float32(1e36 / ratio)                   # large, sums stay finite
+        elif fam[i] == 3:
+            sc[rows] *= np.float32(60.0)                           # exp underflow for most rows
+        elif fam[i] == 4:
+            sc[rows] = np.float32(3.0)                             # equal scores: the mean
+        else:
+            kv[rows] *= np.float32(1e-20)                          # small normals
+    return kv, sc
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("ratio", [2, 4, 128])
+def test_compress_extreme_values(kvq, orc, layout, ratio):
+    rng = np.random.default_rng(63 + ratio)
+    R = 60 if ratio < 128 else 24
+    kv, sc = extreme_windows(rng, ratio, R)
+    cs = wl.rope_cos_sin(max_pos=4096)
+    pos = rng.integers(0, 4096, R).astype(np.int32)
+    slots = wl.distinct_slots(rng, R, 64, NUM_PAGES * 64)
+    pool = kvq.new_pool(layout, NUM_PAGES)
+    kvq.kv_compress_store(pool, layout, to_dev(kv), to_dev(sc), ratio, to_dev(pos), to_dev(cs), to_dev(slots))
+    ref = orc.new_pool(layout, NUM_PAGES)
+    orc.kv_compress_store(layout, ref, kv, sc, ratio, pos, cs, slots)
+    f64, _ = orc.pool_rows(kv, sc, ratio)
+    compare_compressed(to_host(pool), ref, layout, slots, f64, label=f"extreme r{ratio} L{layout}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_compress_state_edges(kvq, orc, layout):
+    """Ratio 4: a window completed at an out-of-pool slot stores nothing but is consumed;
+    out-of-range state ids are skipped; extreme values as in the batch test."""
+    import torch
+    rng = np.random.default_rng(64)
+    ratio, S = 4, 12
+    kv, sc = extreme_windows(rng, ratio, S)          # window of sequence s = rows [4s, 4s+4)
+    cs = wl.rope_cos_sin(max_pos=4096)
+    pos = rng.integers(0, 4096, S).astype(np.int32)
+    slots = wl.distinct_slots(rng, S, 64, NUM_PAGES * 64)
+    slots[5] = NUM_PAGES * 64                         # consumed, stores nothing
+    pool = kvq.new_pool(layout, NUM_PAGES)
+    state, count = kvq.new_compress_state(S)
+    for t in range(ratio):
+        ids = np.arange(S, dtype=np.int32)
+        ids_call = np.concatenate([ids, [-1, S]]).astype(np.int32)   # two skipped rows
+        kv_t = np.concatenate([kv[ids * ratio + t], kv[:2]])
+        sc_t = np.concatenate([sc[ids * ratio + t], sc[:2]])
+        kvq.kv_compress_state_update(pool, layout, state, count, ratio, to_dev(ids_call), to_dev(kv_t),
+                                     to_dev(sc_t), to_dev(np.concatenate([pos, pos[:2]])), to_dev(cs),
+                                     to_dev(np.concatenate([slots, slots[:2]])))
+    torch.cuda.synchronize()
+    assert np.all(to_host(count) == 0)
+    ref = orc.new_pool(layout, NUM_PAGES)
+    orc.kv_compress_store(layout, ref, kv, sc, ratio, pos, cs, slots)
+    valid = slots < NUM_PAGES * 64
+    f64, _ = orc.pool_rows(kv, sc, ratio)
+    got = to_host(pool)
+    compare_compressed(got, ref, layout, slots[valid], f64[valid], label=f"state edges L{layout}")
+    assert untouched_equal(got, ref, layout, slots[valid])
