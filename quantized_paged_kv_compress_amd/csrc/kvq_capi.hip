@@ -90,9 +90,9 @@ int compress_dispatch(int32_t ratio, void* pool, int64_t num_pages, const float*
         case 4: return compress_short<L, 4>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
         case 8: return compress_long<L, 8, 4, 1>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
         case 16: return compress_long<L, 16, 4, 2>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
-        case 32: return compress_long<L, 32, 4, 4>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
-        case 64: return compress_long<L, 64, 4, 4>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
-        case 128: return compress_long<L, 128, 4, 4>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 32: return compress_long<L, 32, 8, 2>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 64: return compress_long<L, 64, 8, 2>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 128: return compress_long<L, 128, 8, 2>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
         default: return KVQ_ERATIO;
     }
 }
