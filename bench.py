@@ -10,10 +10,11 @@ resident in HBM:
   3. C128A: 16384 output rows, ratio 128, fp32 kv/score [2097152, 512], V41 pool.
 Each step touches ~9.1 GB, far beyond the 256 MB last-level cache, so every kernel
 reads cold inputs.  `value` is compressed rows per second over the whole step; every
-kernel's HIP-event time, algorithmic bytes and fraction of the 8 TB/s HBM peak are in
-`kernels`; `roofline` is the dominant kernel (C128A).
+kernel's duration (HIP events recorded by its own dispatch; mean, median, p10, p90),
+algorithmic bytes and fraction of the 8 TB/s HBM peak are in `kernels`; `roofline` is
+the dominant kernel (C128A).
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline] [--no-micro]
 """
 import argparse
 import hashlib
@@ -170,6 +171,30 @@ def micro_bench(kvq, wl, dev, cs, layers=61, reps=20, calls=50):
             "latency_us": table, "swa_hoisting": step}
 
 
+class DispatchTimer:
+    """Pairs of HIP events that a kernel's own dispatch records at its start and end
+    (kvq_profile_next_launch), so elapsed times are kernel durations without the gaps
+    between commands on the stream."""
+
+    def __init__(self, kvq, n):
+        import torch
+        self.kvq = kvq
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+        for a, b in self.ev:      # a torch event gets its HIP handle when first recorded
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+
+    def arm(self, j):
+        self.kvq.profile_next_launch(*self.ev[j])
+
+    def us(self, j):
+        a, b = self.ev[j]
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3
+
+
 def ratio_sweep(kvq, wl, dev, cs, kv, sc, c4_pool, c4_slots, reps=5):
     """NEXT-row measurements on the resident C128A inputs (2,097,152 fp32 rows of kv and
     score): every supported ratio r >= 2 compresses the same input rows into 2,097,152 / r
@@ -182,18 +207,17 @@ def ratio_sweep(kvq, wl, dev, cs, kv, sc, c4_pool, c4_slots, reps=5):
     pool = kvq.new_pool(kvq.V41, num_pages)
     sweep = {}
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    clock = DispatchTimer(kvq, 1)
     for r in (2, 4, 8, 16, 32, 64, 128):
         R = rows_in // r
         pos = torch.from_numpy(rng.integers(0, 65536, R).astype(np.int32)).to(dev)
         slots = torch.from_numpy(wl.distinct_slots(rng, R, 64, num_pages * 64)).to(dev)
         times = []
         for k in range(reps + 1):
-            ev[0].record()
+            clock.arm(0)
             kvq.kv_compress_store(pool, kvq.V41, kv[:R * r], sc[:R * r], r, pos, cs, slots)
-            ev[1].record()
-            ev[1].synchronize()
             if k:
-                times.append(ev[0].elapsed_time(ev[1]) * 1e3)
+                times.append(clock.us(0))
         us = float(np.median(times))
         b = bytes_compress(R, r, kvq.bytes_per_token(kvq.V41))
         sweep[f"r{r}"] = {"rows": R, "us": round(us, 1), "GB/s": round(b / us / 1e3, 1),
@@ -201,12 +225,10 @@ def ratio_sweep(kvq, wl, dev, cs, kv, sc, c4_pool, c4_slots, reps=5):
     out = torch.empty((c4_slots.numel(), HEAD), dtype=torch.bfloat16, device=dev)
     times = []
     for k in range(reps + 1):
-        ev[0].record()
+        clock.arm(0)
         kvq.kv_dequant_slots(c4_pool, kvq.V41, c4_slots, out)
-        ev[1].record()
-        ev[1].synchronize()
         if k:
-            times.append(ev[0].elapsed_time(ev[1]) * 1e3)
+            times.append(clock.us(0))
     us = float(np.median(times))
     n = c4_slots.numel()
     b = n * (4 + kvq.bytes_per_token(kvq.V41) + HEAD * 2)
@@ -237,7 +259,8 @@ def ratio_sweep(kvq, wl, dev, cs, kv, sc, c4_pool, c4_slots, reps=5):
                  kvq.bytes_per_token(kvq.V41))
         decode[f"r{r}"] = {"sequences": S, "us_per_step": round(us / r, 2), "GB/s": round(b / us / 1e3, 1),
                            "frac_of_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
-    return {"method": "HIP events, median of %d launches; the ratio sweep reads the same 8 GiB "
+    return {"method": "HIP events recorded by each launch's own dispatch, median of %d launches "
+                      "(decode steps: stream events around one full window); the ratio sweep reads the same 8 GiB "
                       "of cold inputs at every ratio; decode steps fold one row per sequence into "
                       "its 6 KiB state per call (one full window timed)" % reps,
             "compress_ratio_sweep_v41": sweep, "dequant_slots_c4a_rows": gather,
@@ -247,8 +270,8 @@ def ratio_sweep(kvq, wl, dev, cs, kv, sc, c4_pool, c4_slots, reps=5):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-micro", action="store_true",
                     help="skip the graph-replayed latency table and the hoisting case")
@@ -257,7 +280,7 @@ def main():
     if args.gpus != 1 or world != 1:
         print("bench.py: this path runs on one GPU; every output row depends only on its own "
               "window, so N GPUs would each run this same step on their own share "
-              "(no multi-GPU run is part of this build).", file=sys.stderr)
+              "(this library runs on one GPU; run one process per GPU).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -286,9 +309,18 @@ def main():
     cs = up(cs_host)
     inputs = {}
     cpu_rows_t = {}   # oracle seconds per workload (timed oracle calls only)
+    cpu_1t = {}       # single-thread oracle: (rows, seconds) on the first chunk of each workload
     if not args.no_cpu_baseline:
         import oracle
         oracle.lib()
+        all_threads = oracle.num_threads()
+
+    def oracle_one_thread(fn, rows, key):
+        oracle.set_num_threads(1)
+        t = time.perf_counter()
+        fn()
+        cpu_1t[key] = (rows, time.perf_counter() - t)
+        oracle.set_num_threads(all_threads)
     for name, seed, ratio in (("c4a", 3, 4), ("c128a", 4, 128)):
         R = 16384
         meta = wl.compressor_meta(seed, R)
@@ -308,6 +340,11 @@ def main():
                 t = time.perf_counter()
                 oracle.kv_compress_store(oracle.V41, orc_pool, a, b, ratio, pos_c, cs_host, slots_c)
                 t_orc += time.perf_counter() - t
+                if i0 == 0:
+                    scratch = oracle.new_pool(oracle.V41, meta["num_pages"])
+                    oracle_one_thread(lambda: oracle.kv_compress_store(
+                        oracle.V41, scratch, a, b, ratio, pos_c, cs_host, slots_c), n, name)
+                    del scratch
         cpu_rows_t[name] = t_orc
         del orc_pool
         inputs[name] = dict(R=R, ratio=ratio, kv=kv, sc=sc, pos=up(meta["pos"]),
@@ -326,36 +363,63 @@ def main():
     c4, c128 = inputs["c4a"], inputs["c128a"]
     names = ["translate", "compress_mixed_fp4", "dequant_fp4", "compress_c4a", "compress_c128a"]
 
-    def step(ev=None):
+    # Kernel durations come from events that a kernel's own dispatch records
+    # (kvq_profile_next_launch); each armed launch adds a few microseconds of gap on the
+    # stream, so inside the timed region only C4A and C128A are armed, and the other
+    # kernels' durations come from one more pass of the same steps right after it.  Every
+    # kernel of a timed step is also bracketed by events recorded on the stream (these hold
+    # the gap between commands as well).
+    timed_armed = {3, 4}
+
+    def step(k=None, armed=(), clocks=None, ev=None):
+        def arm(j):
+            if j in armed:
+                clocks[k].arm(j)
         if ev: ev[0].record()
+        arm(0)
         loc = kvq.kv_translate_slots(m["table"], m["full"], m["loc"])
         if ev: ev[1].record()
+        arm(1)
         kvq.kv_compress_store(m["pool"], kvq.V41_FP4, m["kv"], m["sc"], 4, m["pos"], cs, loc)
         if ev: ev[2].record()
+        arm(2)
         kvq.kv_dequant(m["pool"], kvq.V41_FP4, m["page_ids"], m["ws"])
         if ev: ev[3].record()
+        arm(3)
         kvq.kv_compress_store(c4["pool"], kvq.V41, c4["kv"], c4["sc"], 4, c4["pos"], cs, c4["slots"])
         if ev: ev[4].record()
+        arm(4)
         kvq.kv_compress_store(c128["pool"], kvq.V41, c128["kv"], c128["sc"], 128, c128["pos"], cs,
                               c128["slots"])
         if ev: ev[5].record()
 
     for _ in range(args.warmup):
         step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    stream_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    clocks = [DispatchTimer(kvq, len(names)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(events[k])
+        step(k, timed_armed, clocks, stream_ev[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    extra = [DispatchTimer(kvq, len(names)) for _ in range(args.steps)]
+    other = [j for j in range(len(names)) if j not in timed_armed]
+    for k in range(args.steps):
+        step(k, other, extra)
+    torch.cuda.synchronize()
     per = {n: [] for n in names}
-    for ev in events:
+    per_stream = {n: [] for n in names}
+    for k in range(args.steps):
         for j, n in enumerate(names):
-            per[n].append(ev[j].elapsed_time(ev[j + 1]))
+            per[n].append((clocks if j in timed_armed else extra)[k].us(j) * 1e-3)
+            per_stream[n].append(stream_ev[k][j].elapsed_time(stream_ev[k][j + 1]))
     avg_ms = {n: float(np.mean(v)) for n, v in per.items()}
-    log("timed region done: " + ", ".join(f"{n} {avg_ms[n] * 1e3:.1f} us" for n in names))
+    avg_stream_ms = {n: float(np.mean(v)) for n, v in per_stream.items()}
+    log("timed region done: " + ", ".join(f"{n} {avg_ms[n] * 1e3:.1f} us "
+                                          f"({avg_stream_ms[n] * 1e3:.1f} between stream events)"
+                                          for n in names))
 
     # achievable-bandwidth reference (context): a plain 1 GiB device copy
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev).normal_()
@@ -383,7 +447,11 @@ def main():
     kernels = {}
     for n in names:
         gbs = alg[n] / (avg_ms[n] * 1e-3) / 1e9
-        kernels[n] = {"us": round(avg_ms[n] * 1e3, 2), "alg_bytes": alg[n], "GB/s": round(gbs, 1),
+        p10, p50, p90 = (float(np.percentile(per[n], q)) * 1e3 for q in (10, 50, 90))
+        kernels[n] = {"us": round(avg_ms[n] * 1e3, 2), "us_median": round(p50, 2),
+                      "us_p10": round(p10, 2), "us_p90": round(p90, 2),
+                      "us_between_stream_events": round(avg_stream_ms[n] * 1e3, 2),
+                      "alg_bytes": alg[n], "GB/s": round(gbs, 1),
                       "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
         if n in rows:
             kernels[n]["rows/s"] = round(rows[n] / (avg_ms[n] * 1e-3), 1)
@@ -401,21 +469,32 @@ def main():
     # ------------------------------------------------------------ CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
+        def mixed_step():
+            rc, loc_h = oracle.translate_slots(mx["table"], mx["full"], mx["cap"])
+            pool = oracle.new_pool(oracle.V41_FP4, mx["num_pages"])
+            oracle.kv_compress_store(oracle.V41_FP4, pool, mx["kv"], mx["score"], 4, mx["pos"], cs_host,
+                                     loc_h[: mx["R"]].copy())
+            oracle.kv_dequant(oracle.V41_FP4, pool, mx["page_ids"])
+
         t = time.perf_counter()
-        rc, loc_h = oracle.translate_slots(mx["table"], mx["full"], mx["cap"])
-        pool = oracle.new_pool(oracle.V41_FP4, mx["num_pages"])
-        oracle.kv_compress_store(oracle.V41_FP4, pool, mx["kv"], mx["score"], 4, mx["pos"], cs_host,
-                                 loc_h[: mx["R"]].copy())
-        oracle.kv_dequant(oracle.V41_FP4, pool, mx["page_ids"])
+        mixed_step()
         t_mixed = time.perf_counter() - t
+        oracle_one_thread(mixed_step, m["R"], "mixed")
         cpu_step = t_mixed + cpu_rows_t["c4a"] + cpu_rows_t["c128a"]
+        # single thread, projected to the whole step from the timed samples
+        step_1t = cpu_1t["mixed"][1] + sum(cpu_1t[k][1] * 16384 / cpu_1t[k][0] for k in ("c4a", "c128a"))
         cpu = {"value": round(rows_per_step / cpu_step, 1), "unit": "rows/s",
                "cores": oracle.num_threads(), "kind": "oracle",
                "sample": ("the whole step: every row of the mixed FP4 step, C4A and C128A, one run, "
                           "OpenMP over rows; input generation excluded (C128A timed chunk by chunk "
                           "as its inputs are generated)"),
                "seconds": {"mixed_fp4": round(t_mixed, 3), "c4a": round(cpu_rows_t["c4a"], 3),
-                           "c128a": round(cpu_rows_t["c128a"], 3)}}
+                           "c128a": round(cpu_rows_t["c128a"], 3)},
+               "single_thread": {
+                   "value": round(rows_per_step / step_1t, 1), "unit": "rows/s", "cores": 1,
+                   "sample": ("one thread on the whole mixed FP4 step, all 16,384 C4A rows and the "
+                              f"first {cpu_1t['c128a'][0]} C128A rows, projected to the whole step"),
+                   "seconds": {k: round(v[1], 3) for k, v in cpu_1t.items()}}}
         log(f"cpu oracle: {cpu['value']} rows/s on {cpu['cores']} threads ({cpu_step:.2f} s per step)")
 
     out = {
@@ -450,6 +529,11 @@ def main():
         },
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "kernel_timing": ("us: HIP events recorded by the kernel's own dispatch (hipExtLaunchKernel), "
+                          "mean over the timed steps for compress_c4a and compress_c128a, and over "
+                          "one more pass of the same steps right after the timed region for the "
+                          "others; us_between_stream_events: events recorded on the stream between "
+                          "the timed launches, which also hold the gap between commands"),
         "copy_1GiB_GB/s": round(copy_gbs, 1),
         "micro": micro,
         "next_rows": nxt,

@@ -76,6 +76,15 @@ extern "C" {
 #define KVQ_LAYOUT_V41 1     /* fp8 e4m3 codes + ue8m0 scale per 32: 528 B/token     */
 #define KVQ_LAYOUT_V41_FP4 2 /* e2m1 codes + e4m3 scale per 32 (+pad): 288 B/token  */
 
+/* Profiling aid: the next kernel launched by an entry point called on this thread records
+ * start_event when the kernel begins executing and stop_event when it has finished, as
+ * part of its own dispatch (hipExtLaunchKernel), so their elapsed time is the kernel's
+ * duration without the gaps between commands.  Either event may be NULL.  The request is
+ * consumed by that launch; a call that launches nothing (an error, or nothing to do)
+ * leaves it pending.  The events (hipEvent_t, created with timing enabled, on the device
+ * of the launch) stay owned by the caller.  Results are unaffected.  Returns KVQ_OK. */
+int kvq_profile_next_launch(void* start_event, void* stop_event);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* kvq_status_string(int status);
 

@@ -93,6 +93,7 @@ def _load(path):
     vp = ctypes.c_void_p
     sig = {
         "orc_num_threads": (ctypes.c_int, []),
+        "orc_set_num_threads": (None, [ctypes.c_int]),
         "orc_code_row_bytes": (i64, [i32]),
         "orc_scale_row_bytes": (i64, [i32]),
         "orc_bytes_per_token": (i64, [i32]),
@@ -144,6 +145,10 @@ def _ok(rc, what):
 # ------------------------------------------------------------------ scalar helpers
 def num_threads():
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n):
+    lib().orc_set_num_threads(int(n))
 
 
 def code_row_bytes(layout):

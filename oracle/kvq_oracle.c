@@ -33,6 +33,9 @@
 /* Threads the OpenMP loops below use (reported with CPU timings). */
 int orc_num_threads(void) { return omp_get_max_threads(); }
 
+/* Sets that thread count for later calls (n >= 1); used to time a single-thread run. */
+void orc_set_num_threads(int n) { omp_set_num_threads(n < 1 ? 1 : n); }
+
 /* ---------------------------------------------------------------- layout facts */
 /* [P1] section 1: V41 keeps 512 fp8 e4m3 codes and one ue8m0 scale per 32 values
  * (16 scales) = 528 B/token; V41_FP4 keeps 512 e2m1 codes (two per byte, 256 B) and one

@@ -14,7 +14,7 @@ import os
 import torch
 
 __all__ = [
-    "V41", "V41_FP4", "KVQError", "load_library", "bytes_per_token", "page_bytes",
+    "V41", "V41_FP4", "KVQError", "load_library", "profile_next_launch", "bytes_per_token", "page_bytes",
     "code_row_bytes", "scale_row_bytes", "new_pool", "kv_store", "kv_store_rope", "kv_store_norm_rope",
     "kv_compress_store", "kv_compress_state_update", "new_compress_state", "kv_dequant", "kv_dequant_slots", "kv_translate_slots", "SUPPORTED_RATIOS",
 ]
@@ -50,6 +50,8 @@ def load_library() -> ctypes.CDLL:
     i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
     L.kvq_status_string.restype = ctypes.c_char_p
     L.kvq_status_string.argtypes = [ctypes.c_int]
+    L.kvq_profile_next_launch.restype = ctypes.c_int
+    L.kvq_profile_next_launch.argtypes = [vp, vp]
     for q in ("kvq_bytes_per_token", "kvq_page_bytes", "kvq_code_row_bytes", "kvq_scale_row_bytes"):
         getattr(L, q).restype = i64
         getattr(L, q).argtypes = [i32]
@@ -70,6 +72,16 @@ def load_library() -> ctypes.CDLL:
         fn.argtypes = args
     _lib = L
     return L
+
+
+def profile_next_launch(start_event, stop_event):
+    """Make the next kernel launched from this thread record the two torch.cuda.Event
+    objects at its own start and end (they must have been recorded once already, so their
+    handles exist)."""
+    handles = (start_event.cuda_event, stop_event.cuda_event)
+    if not all(handles):
+        raise ValueError("profile_next_launch: record each event once before arming it")
+    load_library().kvq_profile_next_launch(*handles)
 
 
 def _raise(fn: str, status: int):

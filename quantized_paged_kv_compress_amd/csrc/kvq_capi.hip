@@ -4,6 +4,7 @@
 // caller's stream with hipLaunchKernel (whose return code reports a rejected launch
 // without touching the process-wide last-error state).  Nothing allocates, frees or
 // synchronises.  Declarations, argument meaning and error behaviour: include/kvq.h.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -27,6 +28,10 @@ bool known_layout(int32_t layout) {
     return layout == KVQ_LAYOUT_V41 || layout == KVQ_LAYOUT_V41_FP4;
 }
 
+// Events requested by kvq_profile_next_launch for this thread's next launch.
+thread_local hipEvent_t t_start_event = nullptr;
+thread_local hipEvent_t t_stop_event = nullptr;
+
 template <typename... KArgs, typename... Args>
 int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, void* stream, Args... args) {
     static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
@@ -36,8 +41,13 @@ int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, void* stream, Args..
         int j = 0;
         ((ptrs[j++] = const_cast<void*>(static_cast<const void*>(&a))), ...);
     }, vals);
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0,
-                                         static_cast<hipStream_t>(stream));
+    const hipEvent_t e0 = t_start_event, e1 = t_stop_event;
+    t_start_event = t_stop_event = nullptr;
+    const hipError_t e =
+        (e0 || e1) ? hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0,
+                                        static_cast<hipStream_t>(stream), e0, e1, 0)
+                   : hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0,
+                                     static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KVQ_OK : KVQ_ELAUNCH;
 }
 
@@ -100,6 +110,12 @@ int compress_dispatch(int32_t ratio, void* pool, int64_t num_pages, const float*
 }  // namespace
 
 extern "C" {
+
+int kvq_profile_next_launch(void* start_event, void* stop_event) {
+    t_start_event = static_cast<hipEvent_t>(start_event);
+    t_stop_event = static_cast<hipEvent_t>(stop_event);
+    return KVQ_OK;
+}
 
 const char* kvq_status_string(int status) {
     switch (status) {

@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("kv_store", "kv_store_rope", "kv_store_norm_rope", "kv_compress_store",
                  "kv_compress_state_update", "kv_dequant_slots", "kv_dequant",
-                 "kv_translate_slots", "kvq_bytes_per_token", "kvq_page_bytes"):
+                 "kv_translate_slots", "kvq_bytes_per_token", "kvq_page_bytes",
+                 "kvq_profile_next_launch"):
         assert want in names
 
 
@@ -52,6 +53,12 @@ def test_layout_queries(kvq, orc):
     assert kvq.page_bytes(V41) == 33792 and kvq.page_bytes(FP4) == 18432
     assert kvq.bytes_per_token(3) == kvq.KVQ_ELAYOUT
     assert kvq.page_bytes(0) == kvq.KVQ_ELAYOUT
+
+
+def test_profile_request_is_host_only(kvq):
+    """Arming (or disarming, with NULL events) touches no device state."""
+    lib = kvq.load_library()
+    assert lib.kvq_profile_next_launch(None, None) == kvq.KVQ_OK
 
 
 def test_status_strings(kvq):
