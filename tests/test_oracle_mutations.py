@@ -57,6 +57,19 @@ MUTATIONS = [
      ["norm_worked", "norm_mapping"]),
     ("fp4 padding not written", "memset(scale + kHead / kBlock, 0, 16); /* documented padding */",
      "(void)0; /* padding left as it was */", ["addressing"]),
+    ("rope pairs offset by one channel", "float x1 = v[base + i], x2 = v[base + half + i];",
+     "float x1 = v[base + i], x2 = v[base + half + (i + 1) % half];", ["rope_pairs"]),
+    ("softmax max not subtracted", "double w = exp((double)score[(i * ratio + j) * ld + c] - m);",
+     "double w = exp((double)score[(i * ratio + j) * ld + c]); (void)m;", ["pool_mean"]),
+    ("pooled row not rounded to bf16", "v[c] = orc_bf16_to_f32(orc_bf16_from_double(p[c]));",
+     "v[c] = (float)p[c];", ["compress_r1", "compress_pool_rope"]),
+    ("gather row from the wrong slot bits", "int64_t r = slot % kPageRows;", "int64_t r = slot % 32;",
+     ["dequant_slots"]),
+    ("fp4 code sign dropped in dequant", "(code[c / 2] & 15) : (code[c / 2] >> 4)",
+     "(code[c / 2] & 7) : ((code[c / 2] >> 4) & 7)", ["dequant_fp4"]),
+    ("dequant scale rows 16 bytes apart", "const uint8_t* scale = pg + kPageRows * cr + r * sr;",
+     "const uint8_t* scale = pg + kPageRows * cr + r * 16;", ["dequant_fp4", "dequant_slots"]),
+    ("translate maps unknown full slots to 0", "? table[f] : -1;", "? table[f] : 0;", ["translate"]),
 ]
 
 PINS = {
@@ -82,6 +95,11 @@ PINS = {
     "norm_worked": lambda o: pins.test_norm_worked_examples(o, golden),
     "norm_exact": lambda o: pins.test_norm_is_nearest_bf16_of_exact_value(o),
     "norm_mapping": lambda o: pins.test_norm_scale_invariance_and_weight_mapping(o),
+    "compress_r1": lambda o: pins.test_compress_ratio_one_equals_store_rope_of_bf16(o),
+    "compress_pool_rope": lambda o: pins.test_compress_equals_pool_then_store_rope(o),
+    "dequant_slots": lambda o: (pins.test_dequant_slots_matches_page_dequant(o, 1),
+                                pins.test_dequant_slots_matches_page_dequant(o, 2)),
+    "dequant_fp4": lambda o: pins.test_dequant_exhaustive_fp4(o),
 }
 
 
