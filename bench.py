@@ -267,6 +267,144 @@ def ratio_sweep(kvq, wl, dev, cs, kv, sc, c4_pool, c4_slots, reps=5):
             "compress_state_decode_v41": decode}
 
 
+# ---------------------------------------------------------------- rocprofv3 summaries
+# `python bench.py --write-profiles RESULTS` condenses the CSV output of the three
+# profiler runs below (written under RESULTS) into the text summaries in profiles/;
+# bench.py reads `traffic` back from the PMC summary.
+PROFILE_RUNS = {
+    "trace": "rocprofv3 --kernel-trace --stats -f csv -d $RESULTS/prof_trace -o trace -- "
+             "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-micro",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d $RESULTS/pmc_fetch -o fetch -- "
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-micro",
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d $RESULTS/pmc_write -o write -- "
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-micro",
+}
+SHORT_NAMES = {
+    "compress_long_kernel<(kvq::Layout)1, 128": "compress_long<V41, ratio 128> (C128A)",
+    "compress_short_kernel<(kvq::Layout)1, 4>": "compress_short<V41, ratio 4> (C4A)",
+    "compress_short_kernel<(kvq::Layout)2, 4>": "compress_short<V41_FP4, ratio 4> (mixed step)",
+    "dequant_kernel<(kvq::Layout)2": "dequant<V41_FP4> (mixed step)",
+    "translate_kernel": "translate (mixed step)",
+    "__amd_rocclr_copyBuffer": "__amd_rocclr_copyBuffer (1 GiB device copy)",
+}
+COPY_KEY = SHORT_NAMES["__amd_rocclr_copyBuffer"]
+DOM_KEY = SHORT_NAMES["compress_long_kernel<(kvq::Layout)1, 128"]
+C4A_KEY = SHORT_NAMES["compress_short_kernel<(kvq::Layout)1, 4>"]
+
+
+def _short_name(name):
+    for k, v in SHORT_NAMES.items():
+        if k in name:
+            return v
+    return None
+
+
+def _find_csv(results, pattern):
+    import glob
+    found = glob.glob(os.path.join(results, pattern), recursive=True)
+    if not found:
+        raise SystemExit(f"bench.py --write-profiles: no {pattern} under {results}")
+    return found[0]
+
+
+def trace_summary(results):
+    import csv
+    rows = list(csv.DictReader(open(_find_csv(results, "prof_trace/**/trace_kernel_stats.csv"))))
+    lines = [
+        "# rocprofv3 kernel-trace summary: one bench step (mixed V41_FP4 step + C4A + C128A), MI355X",
+        f"# command: {PROFILE_RUNS['trace']}",
+        "# (run from the repository root with TMPDIR=/tmp, RESULTS = the results directory;",
+        "#  summarised by: python bench.py --write-profiles $RESULTS)",
+        "# The bench launches every kernel on torch's current stream; 11 launches of each kernel",
+        "# = 1 warmup step + 5 timed steps + 5 steps of the pass that times the kernels not",
+        "# armed in the timed region.",
+        "",
+        f"{'kernel':<52} {'calls':>5} {'avg_us':>10} {'min_us':>10} {'max_us':>10}",
+    ]
+    for r in rows:
+        name = _short_name(r["Name"])
+        if name is not None:
+            lines.append(f"{name:<52} {int(r['Calls']):>5} {float(r['AverageNs']) / 1e3:>10.2f} "
+                         f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f}")
+    bench_json = os.path.join(results, "bench.json")
+    if os.path.exists(bench_json):
+        b = json.load(open(bench_json))
+        lines += ["", "# bench.py (same build, separate run, default 50 timed steps; HIP events recorded by",
+                  "# each kernel's own dispatch, so without the gaps between commands), mean us per launch:"]
+        for k, v in b["kernels"].items():
+            lines.append(f"#   {k:<22} {v['us']:>10.2f}  ({v['GB/s']} GB/s algorithmic, "
+                         f"{100 * v['frac_of_peak']:.1f} % of 8 TB/s)")
+    return "\n".join(lines) + "\n"
+
+
+def _pmc_per_kernel(path):
+    import csv
+    agg = {}
+    for r in csv.DictReader(open(path)):
+        name = _short_name(r["Kernel_Name"])
+        if name is not None:
+            agg.setdefault(name, []).append((int(r["Grid_Size"]), float(r["Counter_Value"])))
+    return agg
+
+
+def pmc_summary(results):
+    import numpy as np
+    f = _pmc_per_kernel(_find_csv(results, "pmc_fetch/**/fetch_counter_collection.csv"))
+    w = _pmc_per_kernel(_find_csv(results, "pmc_write/**/write_counter_collection.csv"))
+    # the calibration copies are the copyBuffer dispatches that write exactly 1 GiB
+    big = {g for g, v in w[COPY_KEY] if abs(v - 1048576.0) < 1.0}
+    copy_write = float(np.mean([v for g, v in w[COPY_KEY] if g in big]))
+    copy_fetch = float(np.mean([v for g, v in f[COPY_KEY] if g in big]))
+    fs = (1 << 30) / (copy_fetch * 1024)
+    ws = (1 << 30) / (copy_write * 1024)
+    fk = float(np.mean([v for _, v in f[DOM_KEY]]))
+    wk = float(np.mean([v for _, v in w[DOM_KEY]]))
+    lines = [
+        "# rocprofv3 PMC summary: HBM traffic per dispatch, MI355X",
+        f"# command (pass 1): {PROFILE_RUNS['fetch']}",
+        f"# command (pass 2): {PROFILE_RUNS['write']}",
+        "# (run from the repository root with TMPDIR=/tmp, RESULTS = the results directory;",
+        "#  summarised by: python bench.py --write-profiles $RESULTS)",
+        "# Counters are KiB per dispatch, averaged over the dispatches of each kernel.  Each is",
+        "# scaled by what the same counter reads for a plain device copy of known size (the",
+        "# bench's 1 GiB torch copy, __amd_rocclr_copyBuffer): on gfx950 FETCH_SIZE reports",
+        f"# {1 / fs:.3f} of the copy's 1 GiB of reads (scale {fs:.1f}) and WRITE_SIZE {1 / ws:.3f} of its",
+        f"# writes (scale {ws:.1f}).  kernel_source_sha256 identifies the kernel sources these",
+        "# counters were taken on; bench.py reports `traffic` only while the sources still hash to it.",
+        "",
+        f"kernel_source_sha256: {kernel_source_hash()}",
+        f"kernel: {DOM_KEY}",
+        f"FETCH_SIZE_KiB_per_dispatch: {fk:.3f}",
+        f"WRITE_SIZE_KiB_per_dispatch: {wk:.3f}",
+        f"copy_bytes_each_way: {1 << 30}",
+        f"copy_FETCH_SIZE_KiB_per_dispatch: {copy_fetch:.3f}",
+        f"copy_WRITE_SIZE_KiB_per_dispatch: {copy_write:.3f}",
+        "",
+        f"# all kernels of the step (raw KiB per dispatch; scaled bytes = fetch*1024*{fs:.1f} + "
+        f"write*1024*{ws:.1f}):",
+    ]
+    alg = {DOM_KEY: bytes_compress(16384, 128, 528), C4A_KEY: bytes_compress(16384, 4, 528)}
+    for k in f:
+        if k == COPY_KEY:
+            continue
+        fa = float(np.mean([v for _, v in f[k]]))
+        wa = float(np.mean([v for _, v in w[k]])) if k in w else 0.0
+        tot = fa * 1024 * fs + wa * 1024 * ws
+        extra = f"  ({tot / alg[k]:.3f} x algorithmic)" if k in alg else ""
+        lines.append(f"#   {k:<48} fetch {fa:>14.1f}  write {wa:>12.1f}  -> {tot / 1e6:>10.2f} MB{extra}")
+    return "\n".join(lines) + "\n"
+
+
+def write_profiles(results):
+    out = os.path.join(ROOT, "profiles")
+    os.makedirs(out, exist_ok=True)
+    for name, text in (("bench_step_kernel_trace.txt", trace_summary(results)),
+                       ("compress_c128a_v41_pmc.txt", pmc_summary(results))):
+        with open(os.path.join(out, name), "w") as fh:
+            fh.write(text)
+        print(text)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -275,7 +413,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-micro", action="store_true",
                     help="skip the graph-replayed latency table and the hoisting case")
+    ap.add_argument("--write-profiles", metavar="RESULTS",
+                    help="summarise rocprofv3 CSVs under RESULTS into profiles/ and exit (no GPU)")
     args = ap.parse_args()
+    if args.write_profiles:
+        write_profiles(args.write_profiles)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this path runs on one GPU; every output row depends only on its own "
