@@ -23,8 +23,9 @@
  *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
  *    asynchronously on it; no call allocates, frees or synchronises, so every call can
  *    be captured into a hipGraph.
- *  - Calls are stateless and thread-safe.  Two calls that write the same pool slots or
- *    output rows concurrently race (the caller orders them with streams/events).
+ *  - Calls keep no state (apart from the per-thread request of kvq_profile_next_launch)
+ *    and are thread-safe.  Two calls that write the same pool slots or output rows
+ *    concurrently race (the caller orders them with streams/events).
  *  - Host-side validation only: arguments are checked before any launch and an error
  *    returns without enqueuing anything.  Device data is not validated, except that a
  *    row whose slot is outside [0, num_pages*64) or whose position is outside
@@ -82,7 +83,8 @@ extern "C" {
  * duration without the gaps between commands.  Either event may be NULL.  The request is
  * consumed by that launch; a call that launches nothing (an error, or nothing to do)
  * leaves it pending.  The events (hipEvent_t, created with timing enabled, on the device
- * of the launch) stay owned by the caller.  Results are unaffected.  Returns KVQ_OK. */
+ * of the launch) stay owned by the caller.  Results are unaffected.  Meant for eager
+ * timing: do not arm a launch that is being captured into a graph.  Returns KVQ_OK. */
 int kvq_profile_next_launch(void* start_event, void* stop_event);
 
 /* Human-readable name of a status code (static string, never NULL). */
