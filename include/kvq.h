@@ -67,7 +67,8 @@ extern "C" {
 /* ---- status codes -------------------------------------------------------------- */
 #define KVQ_OK 0
 #define KVQ_EINVAL (-1)    /* null pointer with work to do, ld < 512, misaligned
-                              pointer or stride, negative size, max_pos <= 0       */
+                              pointer or stride, negative size, max_pos <= 0,
+                              num_pages > 2^32                                     */
 #define KVQ_ELAYOUT (-2)   /* layout id is not KVQ_LAYOUT_V41 / KVQ_LAYOUT_V41_FP4 */
 #define KVQ_ERATIO (-3)    /* ratio not built (supported: 1, 2, 4, 8, 16, 32, 64, 128) */
 #define KVQ_ECAPACITY (-4) /* kv_translate_slots with n > cap; nothing enqueued   */

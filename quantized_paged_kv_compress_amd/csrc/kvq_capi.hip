@@ -19,6 +19,7 @@ namespace {
 using kvq::Layout;
 
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxPages = int64_t(1) << 32;  // far beyond any pool; keeps num_pages * 64 exact
 constexpr int64_t kDequantLongList = 1024;  // pages; from here on 4 rows per wavefront
 constexpr int32_t kMaxStateRatio = 1 << 20;
 
@@ -160,7 +161,7 @@ static int store_common(int mode, int32_t layout, void* pool, int64_t num_pages,
                         void* stream) {
     const bool rope = mode >= 1, norm = mode == 2;
     if (!known_layout(layout)) return KVQ_ELAYOUT;
-    if (n < 0 || n > kMaxRows || num_pages < 0) return KVQ_EINVAL;
+    if (n < 0 || n > kMaxRows || num_pages < 0 || num_pages > kMaxPages) return KVQ_EINVAL;
     if (rope && max_pos <= 0) return KVQ_EINVAL;
     if (norm && !(eps >= 0.0f && eps < __builtin_huge_valf())) return KVQ_EINVAL;
     if (n == 0) return KVQ_OK;
@@ -203,7 +204,7 @@ int kv_compress_store(int32_t layout, void* pool, int64_t num_pages, const float
     if (ratio != 1 && ratio != 2 && ratio != 4 && ratio != 8 && ratio != 16 && ratio != 32 &&
         ratio != 64 && ratio != 128)
         return KVQ_ERATIO;
-    if (R < 0 || R > kMaxRows || num_pages < 0 || max_pos <= 0) return KVQ_EINVAL;
+    if (R < 0 || R > kMaxRows || num_pages < 0 || num_pages > kMaxPages || max_pos <= 0) return KVQ_EINVAL;
     if (R == 0) return KVQ_OK;
     if (!pool || !kv || (ratio > 1 && !score) || !pos || !cos_sin || !slots) return KVQ_EINVAL;
     if (ld < kvq::kHeadDim || ld % 4 != 0) return KVQ_EINVAL;
@@ -220,7 +221,7 @@ int kv_compress_state_update(int32_t layout, void* pool, int64_t num_pages, floa
                              int64_t max_pos, const int32_t* slots, int64_t n, void* stream) {
     if (!known_layout(layout)) return KVQ_ELAYOUT;
     if (ratio < 1 || ratio > kMaxStateRatio) return KVQ_ERATIO;
-    if (n < 0 || n > kMaxRows || num_pages < 0 || num_states < 0 || max_pos <= 0) return KVQ_EINVAL;
+    if (n < 0 || n > kMaxRows || num_pages < 0 || num_pages > kMaxPages || num_states < 0 || max_pos <= 0) return KVQ_EINVAL;
     if (n == 0) return KVQ_OK;
     if (!pool || !state || !count || !state_ids || !kv || !score || !pos || !cos_sin || !slots)
         return KVQ_EINVAL;
@@ -240,7 +241,7 @@ int kv_compress_state_update(int32_t layout, void* pool, int64_t num_pages, floa
 int kv_dequant(int32_t layout, const void* pool, int64_t num_pages, const int32_t* page_ids,
                int64_t P, uint16_t* out, void* stream) {
     if (!known_layout(layout)) return KVQ_ELAYOUT;
-    if (P < 0 || P > (kMaxRows >> kvq::kPageBits) || num_pages < 0) return KVQ_EINVAL;
+    if (P < 0 || P > (kMaxRows >> kvq::kPageBits) || num_pages < 0 || num_pages > kMaxPages) return KVQ_EINVAL;
     if (P == 0) return KVQ_OK;
     if (!pool || !page_ids || !out) return KVQ_EINVAL;
     if (!aligned16(pool) || !aligned16(out)) return KVQ_EINVAL;
@@ -262,7 +263,7 @@ int kv_dequant(int32_t layout, const void* pool, int64_t num_pages, const int32_
 int kv_dequant_slots(int32_t layout, const void* pool, int64_t num_pages, const int32_t* slots, int64_t n,
                      uint16_t* out, void* stream) {
     if (!known_layout(layout)) return KVQ_ELAYOUT;
-    if (n < 0 || n > kMaxRows || num_pages < 0) return KVQ_EINVAL;
+    if (n < 0 || n > kMaxRows || num_pages < 0 || num_pages > kMaxPages) return KVQ_EINVAL;
     if (n == 0) return KVQ_OK;
     if (!pool || !slots || !out) return KVQ_EINVAL;
     if (!aligned16(pool) || !aligned16(out)) return KVQ_EINVAL;

@@ -218,3 +218,17 @@ def test_product_path_does_not_reference_the_oracle():
         text = open(path).read()
         for b in banned:
             assert b not in text, (path, b)
+
+
+def test_oversized_page_count_is_rejected(kvq):
+    """num_pages above 2^32 is refused by every pool entry point before any launch."""
+    L = kvq.load_library()
+    big = (1 << 32) + 1
+    assert L.kv_store(V41, A, big, B, 512, C, 1, None) == kvq.KVQ_EINVAL
+    assert L.kv_store_rope(V41, A, big, B, 512, C, A, 10, C, 1, None) == kvq.KVQ_EINVAL
+    assert L.kv_store_norm_rope(V41, A, big, B, 512, C, 1e-6, A, B, 10, C, 1, None) == kvq.KVQ_EINVAL
+    assert L.kv_compress_store(V41, A, big, B, C, 512, 4, A, B, 10, C, 5, None) == kvq.KVQ_EINVAL
+    assert L.kv_compress_state_update(V41, A, big, B, C, 8, 4, A, B, C, 512, A, B, 10, C, 3,
+                                      None) == kvq.KVQ_EINVAL
+    assert L.kv_dequant(V41, A, big, B, 1, C, None) == kvq.KVQ_EINVAL
+    assert L.kv_dequant_slots(V41, A, big, B, 1, C, None) == kvq.KVQ_EINVAL
