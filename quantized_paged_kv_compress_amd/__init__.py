@@ -108,6 +108,14 @@ def _dev(t: torch.Tensor, name: str, dtypes) -> torch.Tensor:
     return t
 
 
+def _vec(t: torch.Tensor, name: str, dtypes=(torch.int32,)) -> torch.Tensor:
+    """A device array passed by pointer: elements must be contiguous."""
+    _dev(t, name, dtypes)
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: need a contiguous tensor (pass .contiguous())")
+    return t
+
+
 def _rows(t: torch.Tensor, name: str) -> int:
     """Row stride (elements) of a [rows, >=512] tensor whose channels are contiguous."""
     if t.dim() != 2 or t.shape[1] < HEAD_DIM or t.stride(1) != 1:
@@ -157,7 +165,7 @@ def kv_store(pool, layout, k, slots, stream=None):
     """Quantise bf16 rows k[i, :512] into pool slots slots[i]."""
     num_pages = _pool(pool, layout)
     ld = _rows(_dev(k, "k", _BF16), "k")
-    _dev(slots, "slots", _I32)
+    _vec(slots, "slots")
     n = slots.numel()
     if k.shape[0] < n:
         raise ValueError("k has fewer rows than slots")
@@ -169,8 +177,8 @@ def kv_store_rope(pool, layout, k, pos, cos_sin, slots, stream=None):
     """RoPE on the last 64 channels at pos[i], then quantise into slots[i]."""
     num_pages = _pool(pool, layout)
     ld = _rows(_dev(k, "k", _BF16), "k")
-    _dev(pos, "pos", _I32)
-    _dev(slots, "slots", _I32)
+    _vec(pos, "pos")
+    _vec(slots, "slots")
     _dev(cos_sin, "cos_sin", _F32)
     if not cos_sin.is_contiguous() or cos_sin.dim() != 2 or cos_sin.shape[1] != ROPE_DIM:
         raise ValueError("cos_sin: need a contiguous fp32 [max_pos, 64] tensor")
@@ -190,8 +198,8 @@ def kv_store_norm_rope(pool, layout, k, weight, eps, pos, cos_sin, slots, stream
     _dev(weight, "weight", _BF16)
     if not weight.is_contiguous() or weight.numel() != HEAD_DIM:
         raise ValueError("weight: need a contiguous bf16 [512] tensor")
-    _dev(pos, "pos", _I32)
-    _dev(slots, "slots", _I32)
+    _vec(pos, "pos")
+    _vec(slots, "slots")
     _dev(cos_sin, "cos_sin", _F32)
     if not cos_sin.is_contiguous() or cos_sin.dim() != 2 or cos_sin.shape[1] != ROPE_DIM:
         raise ValueError("cos_sin: need a contiguous fp32 [max_pos, 64] tensor")
@@ -211,8 +219,8 @@ def kv_compress_store(pool, layout, kv, score, ratio, pos, cos_sin, slots, strea
     if score is not None:
         if _rows(_dev(score, "score", _F32), "score") != ld or score.shape[0] != kv.shape[0]:
             raise ValueError("score must match kv in shape and stride")
-    _dev(pos, "pos", _I32)
-    _dev(slots, "slots", _I32)
+    _vec(pos, "pos")
+    _vec(slots, "slots")
     _dev(cos_sin, "cos_sin", _F32)
     if not cos_sin.is_contiguous() or cos_sin.dim() != 2 or cos_sin.shape[1] != ROPE_DIM:
         raise ValueError("cos_sin: need a contiguous fp32 [max_pos, 64] tensor")
@@ -236,7 +244,7 @@ def kv_compress_state_update(pool, layout, state, count, ratio, state_ids, kv, s
     stored at slots[j] with RoPE at pos[j].  At most one row per state per call."""
     num_pages = _pool(pool, layout)
     _dev(state, "state", _F32)
-    _dev(count, "count", _I32)
+    _vec(count, "count")
     if not state.is_contiguous() or state.dim() != 3 or tuple(state.shape[1:]) != (3, HEAD_DIM):
         raise ValueError("state: need a contiguous fp32 [num_states, 3, 512] tensor")
     if count.numel() != state.shape[0]:
@@ -245,7 +253,7 @@ def kv_compress_state_update(pool, layout, state, count, ratio, state_ids, kv, s
     if _rows(_dev(score, "score", _F32), "score") != ld or score.shape[0] != kv.shape[0]:
         raise ValueError("score must match kv in shape and stride")
     for t, nm in ((state_ids, "state_ids"), (pos, "pos"), (slots, "slots")):
-        _dev(t, nm, _I32)
+        _vec(t, nm)
     _dev(cos_sin, "cos_sin", _F32)
     if not cos_sin.is_contiguous() or cos_sin.dim() != 2 or cos_sin.shape[1] != ROPE_DIM:
         raise ValueError("cos_sin: need a contiguous fp32 [max_pos, 64] tensor")
@@ -261,7 +269,7 @@ def kv_compress_state_update(pool, layout, state, count, ratio, state_ids, kv, s
 def kv_dequant(pool, layout, page_ids, out=None, stream=None):
     """bf16 [P*64, 512] workspace of the listed pages (list order)."""
     num_pages = _pool(pool, layout)
-    _dev(page_ids, "page_ids", _I32)
+    _vec(page_ids, "page_ids")
     P = page_ids.numel()
     if out is None:
         out = torch.empty((P * PAGE_ROWS, HEAD_DIM), dtype=torch.bfloat16, device=pool.device)
@@ -276,7 +284,7 @@ def kv_dequant(pool, layout, page_ids, out=None, stream=None):
 def kv_dequant_slots(pool, layout, slots, out=None, stream=None):
     """bf16 [n, 512]: the dequantised rows at slots[i] (rows of out-of-pool slots untouched)."""
     num_pages = _pool(pool, layout)
-    _dev(slots, "slots", _I32)
+    _vec(slots, "slots")
     n = slots.numel()
     if out is None:
         out = torch.empty((n, HEAD_DIM), dtype=torch.bfloat16, device=pool.device)
@@ -293,9 +301,9 @@ def kv_translate_slots(table, full_loc, out, stream=None):
 
     Returns out[:n], or None when full_loc is longer than out (nothing is written; the
     caller then translates into a buffer of its own, still once per step)."""
-    _dev(table, "table", _I32)
-    _dev(full_loc, "full_loc", _I32)
-    _dev(out, "out", _I32)
+    _vec(table, "table")
+    _vec(full_loc, "full_loc")
+    _vec(out, "out")
     n = full_loc.numel()
     st = load_library().kv_translate_slots(_ptr(table), table.numel(), _ptr(full_loc), n,
                                            _ptr(out), out.numel(), _stream(stream))

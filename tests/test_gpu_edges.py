@@ -148,3 +148,21 @@ def test_compress_state_edges(kvq, orc, layout):
     got = to_host(pool)
     compare_compressed(got, ref, layout, slots[valid], f64[valid], label=f"state edges L{layout}")
     assert untouched_equal(got, ref, layout, slots[valid])
+
+
+def test_binding_rejects_strided_index_arrays(kvq):
+    """Index arrays are passed by pointer, so a strided view is refused, not misread."""
+    import torch
+    pool = kvq.new_pool(V41, 4)
+    k = torch.zeros((8, 512), dtype=torch.bfloat16, device="cuda")
+    idx = torch.arange(64, 80, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        kvq.kv_store(pool, V41, k, idx[::2])
+    with pytest.raises(ValueError):
+        kvq.kv_dequant(pool, V41, torch.zeros(8, dtype=torch.int32, device="cuda")[::2])
+    table = torch.arange(128, dtype=torch.int32, device="cuda")
+    out = torch.empty(16, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        kvq.kv_translate_slots(table, idx[::2], out)
+    kvq.kv_store(pool, V41, k, idx[::2].contiguous())       # the same data, contiguous: fine
+    torch.cuda.synchronize()
