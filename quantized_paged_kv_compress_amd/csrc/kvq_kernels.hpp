@@ -173,14 +173,23 @@ __global__ __launch_bounds__(kWave * kWaves) void compress_long_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) { m[e] = -__builtin_inff(); l[e] = 0.0f; acc[e] = 0.0f; }
 
-    float xa[kChunk][8], sa[kChunk][8], xb[kChunk][8], sb[kChunk][8];
-    load_chunk<kChunk>(kv, score, base, ld, lane, xa, sa);
+    if constexpr (kChunksPerWave <= 4) {
+        // the wavefront's whole share fits in registers: issue every load, then fold
+        float x[kChunksPerWave][kChunk][8], sc[kChunksPerWave][kChunk][8];
+#pragma unroll
+        for (int c = 0; c < kChunksPerWave; ++c) load_chunk<kChunk>(kv, score, base + c * step, ld, lane, x[c], sc[c]);
+#pragma unroll
+        for (int c = 0; c < kChunksPerWave; ++c) fold_chunk<kChunk>(x[c], sc[c], m, l, acc);
+    } else {
+        float xa[kChunk][8], sa[kChunk][8], xb[kChunk][8], sb[kChunk][8];
+        load_chunk<kChunk>(kv, score, base, ld, lane, xa, sa);
 #pragma unroll 1
-    for (int c = 0; c < kChunksPerWave; c += 2) {
-        load_chunk<kChunk>(kv, score, base + (c + 1) * step, ld, lane, xb, sb);
-        fold_chunk<kChunk>(xa, sa, m, l, acc);
-        if (c + 2 < kChunksPerWave) load_chunk<kChunk>(kv, score, base + (c + 2) * step, ld, lane, xa, sa);
-        fold_chunk<kChunk>(xb, sb, m, l, acc);
+        for (int c = 0; c < kChunksPerWave; c += 2) {
+            load_chunk<kChunk>(kv, score, base + (c + 1) * step, ld, lane, xb, sb);
+            fold_chunk<kChunk>(xa, sa, m, l, acc);
+            if (c + 2 < kChunksPerWave) load_chunk<kChunk>(kv, score, base + (c + 2) * step, ld, lane, xa, sa);
+            fold_chunk<kChunk>(xb, sb, m, l, acc);
+        }
     }
 
     RopeCS cs;
