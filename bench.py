@@ -171,6 +171,18 @@ def micro_bench(kvq, wl, dev, cs, layers=61, reps=20, calls=50):
             "latency_us": table, "swa_hoisting": step}
 
 
+def device_facts(torch):
+    """What the runtime reports about the GPU the bench ran on."""
+    p = torch.cuda.get_device_properties(0)
+    facts = {"name": p.name, "compute_units": p.multi_processor_count,
+             "memory_GiB": round(p.total_memory / 2 ** 30, 1)}
+    for key, attr in (("arch", "gcnArchName"), ("l2_bytes", "L2_cache_size"),
+                      ("max_shared_memory_per_block", "shared_memory_per_block")):
+        if hasattr(p, attr):
+            facts[key] = getattr(p, attr)
+    return facts
+
+
 class DispatchTimer:
     """Pairs of HIP events that a kernel's own dispatch records at its start and end
     (kvq_profile_next_launch), so elapsed times are kernel durations without the gaps
@@ -671,6 +683,7 @@ def main():
             "traffic": None if traffic is None else round(traffic["bytes"]),
         },
         "cpu_baseline": cpu,
+        "device": device_facts(torch),
         "kernels": kernels,
         "kernel_timing": ("us: HIP events recorded by the kernel's own dispatch (hipExtLaunchKernel), "
                           "mean over the timed steps for compress_c4a and compress_c128a, and over "
