@@ -322,8 +322,9 @@ def test_c4a_full_size_sampled(kvq, orc, cos_sin, cos_sin_dev, layout):
 
 
 @pytest.mark.slow
-def test_c128a_full_size_sampled(kvq, orc, cos_sin, cos_sin_dev):
-    sampled_compressor_check(kvq, orc, V41, 128, 16384, 4, 96, cos_sin, cos_sin_dev)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_c128a_full_size_sampled(kvq, orc, cos_sin, cos_sin_dev, layout):
+    sampled_compressor_check(kvq, orc, layout, 128, 16384, 4, 96, cos_sin, cos_sin_dev)
 
 
 # ------------------------------------------------------------------ decode-step state
