@@ -64,3 +64,68 @@ def test_graph_replay_matches_eager():
         got = [to_host(x) for x in (loc, pool_a, pool_b, ws)]
         for name, a, b in zip(("translate", "store_rope", "compress", "dequant"), got, want):
             assert np.array_equal(a, b), (rep, name)
+
+
+def test_graph_replay_of_norm_gather_and_decode_state():
+    """The remaining entry points in one graph: K-norm store, token-gather dequant and the
+    decode-step compressor state.  Each replay is one decode step whose new rows are copied
+    into the captured input buffers first; after every replay the pools, state, counts and
+    gathered rows must equal the same steps run eagerly."""
+    import torch
+    kvq = gpu_lib()
+    rng = np.random.default_rng(42)
+    cs = to_dev(wl.rope_cos_sin(max_pos=4096))
+    S, ratio, num_pages, steps = 48, 4, 8, 6
+    w = to_dev(wl.bf16_bits(rng.uniform(0.5, 1.5, 512).astype(np.float32)))
+    step_kv = [rng.standard_normal((S, 512)).astype(np.float32) for _ in range(steps)]
+    step_sc = [(2 * rng.standard_normal((S, 512))).astype(np.float32) for _ in range(steps)]
+    step_k = [wl.bf16_bits(rng.standard_normal((S, 512)).astype(np.float32)) for _ in range(steps)]
+    ids = to_dev(rng.permutation(S).astype(np.int32))
+    pos = to_dev(rng.integers(0, 4096, S).astype(np.int32))
+    slots_c = to_dev(wl.distinct_slots(rng, S, 64, num_pages * 64))
+    slots_k = to_dev(wl.distinct_slots(rng, S, 64, num_pages * 64))
+
+    def make():
+        st, cnt = kvq.new_compress_state(S)
+        return dict(pool_c=kvq.new_pool(V41, num_pages), pool_k=kvq.new_pool(FP4, num_pages),
+                    state=st, count=cnt,
+                    gathered=torch.zeros((S, 512), dtype=torch.bfloat16, device="cuda"),
+                    kv=torch.empty((S, 512), dtype=torch.float32, device="cuda"),
+                    sc=torch.empty((S, 512), dtype=torch.float32, device="cuda"),
+                    k=torch.empty((S, 512), dtype=torch.int16, device="cuda"))
+
+    def seq(b):
+        kvq.kv_store_norm_rope(b["pool_k"], FP4, b["k"], w, 1e-6, pos, cs, slots_k)
+        kvq.kv_compress_state_update(b["pool_c"], V41, b["state"], b["count"], ratio, ids, b["kv"], b["sc"],
+                                     pos, cs, slots_c)
+        kvq.kv_dequant_slots(b["pool_c"], V41, slots_c, b["gathered"])
+
+    def feed(b, t):
+        b["kv"].copy_(torch.from_numpy(step_kv[t]))
+        b["sc"].copy_(torch.from_numpy(step_sc[t]))
+        b["k"].copy_(torch.from_numpy(step_k[t].view(np.int16)))
+
+    eager, graphed = make(), make()
+    # capture on a side stream after a warm-up call on a scratch set of buffers
+    warm = make()
+    feed(warm, 0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        seq(warm)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        seq(graphed)
+    keys = ("pool_k", "pool_c", "state", "count", "gathered")
+    for t in range(steps):
+        feed(eager, t)
+        seq(eager)
+        feed(graphed, t)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for key in keys:
+            assert np.array_equal(to_host(graphed[key]), to_host(eager[key])), (t, key)
+    assert np.all(to_host(eager["count"]) == steps % ratio)
