@@ -83,6 +83,64 @@ def read_traffic(duration_key_bytes):
         return None
 
 
+def graph_us(fn, n_calls, reps=20):
+    """Median per-call microseconds of `n_calls` back-to-back calls of fn captured in one
+    HIP graph (torch.cuda.CUDAGraph), over `reps` replays."""
+    import numpy as np
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n_calls):
+            fn()
+    for _ in range(3):
+        g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(reps):
+        e0.record()
+        g.replay()
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / n_calls)
+    return float(np.median(times))
+
+
+def store_configs(kvq, wl, dev, cs, reps=20, calls=50):
+    """The two store workloads at their own sizes: V41 plain store (64 tokens, 16-page pool)
+    and V41 store + RoPE (512 tokens, 4096-page pool).  Under 1 MB of data each, so the
+    time is launch latency: graph-replayed per-launch time, tokens/s and algorithmic GB/s."""
+    import numpy as np
+    import torch
+
+    def t(a):
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    out = {"method": f"HIP graph of {calls} back-to-back launches, median of {reps} replays"}
+    d1 = wl.store_v41(seed=1)
+    pool1 = kvq.new_pool(kvq.V41, d1["num_pages"])
+    k1, s1 = t(d1["k"]), t(d1["slots"])
+    d2 = wl.store_rope(seed=2)
+    pool2 = kvq.new_pool(kvq.V41, d2["num_pages"])
+    k2, p2, s2 = t(d2["k"]), t(d2["pos"]), t(d2["slots"])
+    cases = (("v41_plain_store", 64, 64 * (1024 + 4 + 528),
+              lambda: kvq.kv_store(pool1, kvq.V41, k1, s1)),
+             ("v41_store_rope", 512, 512 * (1024 + 4 + 4 + 256 + 528),
+              lambda: kvq.kv_store_rope(pool2, kvq.V41, k2, p2, cs, s2)))
+    for name, n, b, fn in cases:
+        us = graph_us(fn, calls, reps)
+        out[name] = {"tokens": n, "us_per_launch": round(us, 3), "tokens/s": round(n / (us * 1e-6), 1),
+                     "alg_bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1)}
+    return out
+
+
 def micro_bench(kvq, wl, dev, cs, layers=61, reps=20, calls=50):
     """Graph-replayed per-launch latency of the kernels in P1's latency table (store,
     store+RoPE, fused K norm+RoPE, c1, c2 at 1/8/64/512 tokens, V41, hot inputs), and the
@@ -91,29 +149,6 @@ def micro_bench(kvq, wl, dev, cs, layers=61, reps=20, calls=50):
     translation inside every layer."""
     import numpy as np
     import torch
-
-    def graph_us(fn, n_calls):
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            fn()
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(n_calls):
-                fn()
-        for _ in range(3):
-            g.replay()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        times = []
-        for _ in range(reps):
-            e0.record()
-            g.replay()
-            e1.record()
-            e1.synchronize()
-            times.append(e0.elapsed_time(e1) * 1e3 / n_calls)
-        return float(np.median(times))
 
     def t(a):
         if a.dtype == np.uint16:
@@ -139,7 +174,7 @@ def micro_bench(kvq, wl, dev, cs, layers=61, reps=20, calls=50):
             "c2": lambda: kvq.kv_compress_store(pool, kvq.V41, kv, sc, 2, pos, cs, slots),
         }
         for name, fn in fns.items():
-            table.setdefault(name, {})[f"bs{bs}"] = round(graph_us(fn, calls), 3)
+            table.setdefault(name, {})[f"bs{bs}"] = round(graph_us(fn, calls, reps), 3)
 
     # P2: translate once per step vs once per layer, 512 new tokens, `layers` layers
     n, cap = 512, 4096
@@ -164,8 +199,8 @@ def micro_bench(kvq, wl, dev, cs, layers=61, reps=20, calls=50):
             kvq.kv_store_rope(p, kvq.V41, k, pos, cs, loc)
 
     step = {"layers": layers, "tokens": n,
-            "hoisted_us_per_step": round(graph_us(hoisted, 1), 2),
-            "per_layer_translate_us_per_step": round(graph_us(per_layer, 1), 2)}
+            "hoisted_us_per_step": round(graph_us(hoisted, 1, reps), 2),
+            "per_layer_translate_us_per_step": round(graph_us(per_layer, 1, reps), 2)}
     return {"method": f"HIP graph of {calls} back-to-back launches, median of {reps} replays, "
                       "per-launch microseconds, V41, hot inputs",
             "latency_us": table, "swa_hoisting": step}
@@ -614,8 +649,10 @@ def main():
     dom = "compress_c128a"
     traffic = read_traffic(alg[dom])
 
-    micro = nxt = None
+    micro = nxt = stores = None
     if not args.no_micro:
+        stores = store_configs(kvq, wl, dev, cs)
+        log(f"store configs: {stores}")
         micro = micro_bench(kvq, wl, dev, cs)
         log(f"micro: {micro['latency_us']}; hoisting {micro['swa_hoisting']}")
         nxt = ratio_sweep(kvq, wl, dev, cs, c128["kv"], c128["sc"], c4["pool"], c4["slots"])
@@ -691,7 +728,14 @@ def main():
                           "others; us_between_stream_events: events recorded on the stream between "
                           "the timed launches, which also hold the gap between commands"),
         "copy_1GiB_GB/s": round(copy_gbs, 1),
+        "store_configs": stores,
         "micro": micro,
+        "pages_context": {
+            "note": "the pages' own figures, measured on other hardware: context, not targets",
+            "store_bs512_us": "1.49 -> 1.39 (hardware not stated)",
+            "c4a_us_gb200": 89.685, "c128a_us_gb200": 1606.181,
+            "c4a_us_here": kernels["compress_c4a"]["us"], "c128a_us_here": kernels[dom]["us"],
+        },
         "next_rows": nxt,
         "c4a": {"rows/s": kernels["compress_c4a"]["rows/s"], "GB/s": kernels["compress_c4a"]["GB/s"],
                 "frac_of_peak": kernels["compress_c4a"]["frac_of_peak"]},
