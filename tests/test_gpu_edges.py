@@ -166,3 +166,46 @@ def test_binding_rejects_strided_index_arrays(kvq):
         kvq.kv_translate_slots(table, idx[::2], out)
     kvq.kv_store(pool, V41, k, idx[::2].contiguous())       # the same data, contiguous: fine
     torch.cuda.synchronize()
+
+
+def test_pool_larger_than_4gib(kvq, orc, cs_small):
+    """Byte offsets past 2^32: rows stored in the last pages of a 4.4 GB V41 pool (and
+    around the 4 GiB mark) equal the oracle's rows, as do the page dequant and the gather."""
+    import torch
+    num_pages = (1 << 17) + 64                       # 131,136 pages x 33,792 B = 4.43 GB
+    pool = kvq.new_pool(V41, num_pages)
+    assert pool.numel() > 1 << 32
+    boundary_page = (1 << 32) // 33792               # the page that straddles byte 2^32
+    pages = np.array([boundary_page - 1, boundary_page, boundary_page + 1, num_pages - 2,
+                      num_pages - 1], np.int64)
+    rng = np.random.default_rng(66)
+    slots = np.concatenate([p * 64 + rng.choice(64, 8, replace=False) for p in pages]).astype(np.int32)
+    n = slots.size
+    k = wl.bf16_bits(rng.standard_normal((n, 512)).astype(np.float32))
+    pos = rng.integers(0, 100, n).astype(np.int32)
+    kvq.kv_store_rope(pool, V41, to_dev(k), to_dev(pos), to_dev(cs_small), to_dev(slots))
+    # the oracle works on a small pool holding the same pages in the same order
+    local = {int(p): i for i, p in enumerate(pages)}
+    small_slots = np.array([local[int(s) >> 6] * 64 + (int(s) & 63) for s in slots], np.int32)
+    ref = orc.new_pool(V41, pages.size)
+    orc.kv_store_rope(V41, ref, k, pos, cs_small, small_slots)
+    got = to_host(pool[torch.from_numpy(pages).to("cuda")])
+    assert np.array_equal(got, ref)
+    # page dequant and token gather read the same far rows back
+    out = kvq.kv_dequant(pool, V41, to_dev(pages.astype(np.int32)))
+    assert np.array_equal(to_host(out).view(np.uint16), orc.kv_dequant(V41, ref, np.arange(pages.size, dtype=np.int32)))
+    g = kvq.kv_dequant_slots(pool, V41, to_dev(slots))
+    ref_g = np.zeros((n, 512), np.uint16)
+    orc.kv_dequant_slots(V41, ref, small_slots, ref_g)
+    assert np.array_equal(to_host(g).view(np.uint16), ref_g)
+    # a ratio-4 compressor writing to the same far slots
+    kv = rng.standard_normal((n * 4, 512)).astype(np.float32)
+    sc = (2 * rng.standard_normal((n * 4, 512))).astype(np.float32)
+    kvq.kv_compress_store(pool, V41, to_dev(kv), to_dev(sc), 4, to_dev(pos), to_dev(cs_small), to_dev(slots))
+    ref2 = orc.new_pool(V41, pages.size)
+    orc.kv_compress_store(V41, ref2, kv, sc, 4, pos, cs_small, small_slots)
+    f64, _ = orc.pool_rows(kv, sc, 4)
+    got2 = to_host(pool[torch.from_numpy(pages).to("cuda")])
+    compare_compressed(got2, ref2, V41, small_slots, f64, label="pool > 4 GiB")
+    del pool
+    torch.cuda.empty_cache()
