@@ -112,7 +112,8 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_short_kernel(
 // chunks w, w + kWaves, ...), so the whole workgroup sweeps its window front to back
 // together -- measured on MI355X about 3 % faster than giving each wavefront a contiguous
 // slice.  Each wavefront double-buffers its chunks (the next chunk's loads are in flight
-// while the current one is folded in) and keeps a per-channel online softmax state --
+// while the current one is folded in; a share of at most four chunks is loaded whole
+// before folding, which measured faster at ratio 64) and keeps a per-channel online softmax state --
 // running max m (log2 units), denominator l, numerator acc -- rescaling once per chunk
 // (the online form of the vLLM page's section 2).  The kWaves partial states are merged
 // through LDS by wavefront 0 -- the only LDS use in the library -- which then rounds,
