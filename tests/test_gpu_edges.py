@@ -209,3 +209,38 @@ def test_pool_larger_than_4gib(kvq, orc, cs_small):
     compare_compressed(got2, ref2, V41, small_slots, f64, label="pool > 4 GiB")
     del pool
     torch.cuda.empty_cache()
+
+
+def test_empty_inputs_through_the_binding(kvq, cs_small):
+    """Zero rows is a no-op for every writer (the pool keeps its canary bytes), empty page or
+    slot lists give empty workspaces, and translate with n = 0 still zeroes its buffer."""
+    import torch
+    dev = "cuda"
+    for layout in LAYOUTS:
+        pool, ref = canary(kvq, layout)
+        k0 = torch.empty((0, 512), dtype=torch.bfloat16, device=dev)
+        i0 = torch.empty(0, dtype=torch.int32, device=dev)
+        f0 = torch.empty((0, 512), dtype=torch.float32, device=dev)
+        w = torch.ones(512, dtype=torch.bfloat16, device=dev)
+        cs = to_dev(cs_small)
+        kvq.kv_store(pool, layout, k0, i0)
+        kvq.kv_store_rope(pool, layout, k0, i0, cs, i0)
+        kvq.kv_store_norm_rope(pool, layout, k0, w, 1e-6, i0, cs, i0)
+        for ratio in (1, 4, 128):
+            kvq.kv_compress_store(pool, layout, f0, f0 if ratio > 1 else None, ratio, i0, cs, i0)
+        state, count = kvq.new_compress_state(3)
+        kvq.kv_compress_state_update(pool, layout, state, count, 4, i0, f0, f0, i0, cs, i0)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(pool), ref)
+        assert not to_host(state).any() and not to_host(count).any()
+        assert tuple(kvq.kv_dequant(pool, layout, i0).shape) == (0, 512)
+        assert tuple(kvq.kv_dequant_slots(pool, layout, i0).shape) == (0, 512)
+    table = torch.arange(100, dtype=torch.int32, device=dev)
+    out = torch.full((16,), 7, dtype=torch.int32, device=dev)
+    got = kvq.kv_translate_slots(table, torch.empty(0, dtype=torch.int32, device=dev), out)
+    torch.cuda.synchronize()
+    assert got.numel() == 0 and np.all(to_host(out) == 0)
+    out.fill_(7)
+    assert kvq.kv_translate_slots(table, torch.arange(17, dtype=torch.int32, device=dev), out) is None
+    torch.cuda.synchronize()
+    assert np.all(to_host(out) == 7)                    # refused: nothing written
