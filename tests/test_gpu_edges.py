@@ -244,3 +244,58 @@ def test_empty_inputs_through_the_binding(kvq, cs_small):
     assert kvq.kv_translate_slots(table, torch.arange(17, dtype=torch.int32, device=dev), out) is None
     torch.cuda.synchronize()
     assert np.all(to_host(out) == 7)                    # refused: nothing written
+
+
+def test_concurrent_host_threads_on_separate_streams(kvq, cs_small):
+    """Calls are thread-safe: four host threads (ctypes releases the GIL during each call)
+    launch compressions and stores into their own pools on their own streams, repeatedly;
+    every pool equals the result of the same calls made from one thread."""
+    import threading
+    import torch
+    rng = np.random.default_rng(71)
+    jobs = []
+    for t in range(4):
+        R, ratio = 300 + 37 * t, (4, 128, 2, 1)[t]
+        kv = to_dev(rng.standard_normal((R * ratio, 512)).astype(np.float32))
+        sc = to_dev((2 * rng.standard_normal((R * ratio, 512))).astype(np.float32))
+        k = to_dev(wl.bf16_bits(rng.standard_normal((R, 512)).astype(np.float32)))
+        pos = to_dev(rng.integers(0, 100, R).astype(np.int32))
+        slots = to_dev(wl.distinct_slots(rng, R, 64, 40 * 64))
+        slots2 = to_dev(wl.distinct_slots(rng, R, 64, 40 * 64))
+        jobs.append((ratio, kv, sc, k, pos, slots, slots2))
+    cs = to_dev(cs_small)
+
+    def run(job, pool_a, pool_b, stream, reps):
+        ratio, kv, sc, k, pos, slots, slots2 = job
+        with torch.cuda.stream(stream):
+            for _ in range(reps):
+                kvq.kv_compress_store(pool_a, V41, kv, sc if ratio > 1 else None, ratio, pos, cs, slots)
+                kvq.kv_store_rope(pool_b, FP4, k, pos, cs, slots2)
+
+    want = []
+    for job in jobs:
+        a, b = kvq.new_pool(V41, 40), kvq.new_pool(FP4, 40)
+        run(job, a, b, torch.cuda.current_stream(), 1)
+        want.append((a, b))
+    torch.cuda.synchronize()
+    got = [(kvq.new_pool(V41, 40), kvq.new_pool(FP4, 40)) for _ in jobs]
+    streams = [torch.cuda.Stream() for _ in jobs]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(i):
+        try:
+            run(jobs[i], got[i][0], got[i][1], streams[i], 20)
+            streams[i].synchronize()
+        except Exception as e:   # reported below, in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(jobs))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for (ga, gb), (wa, wb) in zip(got, want):
+        assert torch.equal(ga, wa) and torch.equal(gb, wb)
