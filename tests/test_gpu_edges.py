@@ -299,3 +299,23 @@ def test_concurrent_host_threads_on_separate_streams(kvq, cs_small):
     assert not errors, errors
     for (ga, gb), (wa, wb) in zip(got, want):
         assert torch.equal(ga, wa) and torch.equal(gb, wb)
+
+
+@pytest.mark.parametrize("ratio", [4, 16, 128])
+@pytest.mark.parametrize("sigma", [0.01, 10.0, 300.0])
+def test_compress_score_spread(kvq, orc, ratio, sigma):
+    """Score spreads far from the workload's sd 2: nearly uniform weights (0.01), sharp
+    (10) and winner-take-all windows (300, where exp underflows for all but a few rows)."""
+    rng = np.random.default_rng(int(80 + ratio + sigma))
+    R = 64 if ratio < 128 else 24
+    kv = rng.standard_normal((R * ratio, 512)).astype(np.float32)
+    sc = (sigma * rng.standard_normal((R * ratio, 512))).astype(np.float32)
+    cs = wl.rope_cos_sin(max_pos=4096)
+    pos = rng.integers(0, 4096, R).astype(np.int32)
+    slots = wl.distinct_slots(rng, R, 64, NUM_PAGES * 64)
+    pool = kvq.new_pool(V41, NUM_PAGES)
+    kvq.kv_compress_store(pool, V41, to_dev(kv), to_dev(sc), ratio, to_dev(pos), to_dev(cs), to_dev(slots))
+    ref = orc.new_pool(V41, NUM_PAGES)
+    orc.kv_compress_store(V41, ref, kv, sc, ratio, pos, cs, slots)
+    f64, _ = orc.pool_rows(kv, sc, ratio)
+    compare_compressed(to_host(pool), ref, V41, slots, f64, label=f"spread {sigma} r{ratio}")
