@@ -242,6 +242,32 @@ class DispatchTimer:
         return a.elapsed_time(b) * 1e3
 
 
+def fp4_configs(kvq, inputs, cs, reps=10):
+    """C4A and C128A with the V41_FP4 layout: the same resident inputs, FP4 pools.  Each
+    repetition runs C4A then C128A, so every C4A launch follows 8 GiB of other traffic and
+    reads cold inputs.  Kernel durations from dispatch-recorded events, mean of `reps`."""
+    import numpy as np
+    clock = DispatchTimer(kvq, 1)
+    pools = {n: kvq.new_pool(kvq.V41_FP4, inputs[n]["pool"].shape[0]) for n in ("c4a", "c128a")}
+    times = {n: [] for n in pools}
+    for k in range(reps + 1):
+        for n in ("c4a", "c128a"):
+            d = inputs[n]
+            clock.arm(0)
+            kvq.kv_compress_store(pools[n], kvq.V41_FP4, d["kv"], d["sc"], d["ratio"], d["pos"], cs, d["slots"])
+            if k:
+                times[n].append(clock.us(0))
+    out = {"method": f"HIP events recorded by each launch's own dispatch, mean of {reps}"}
+    for n, t in times.items():
+        d = inputs[n]
+        us = float(np.mean(t))
+        b = bytes_compress(d["R"], d["ratio"], kvq.bytes_per_token(kvq.V41_FP4))
+        out[n] = {"rows": d["R"], "ratio": d["ratio"], "us": round(us, 2), "alg_bytes": b,
+                  "GB/s": round(b / us / 1e3, 1), "frac_of_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                  "rows/s": round(d["R"] / (us * 1e-6), 1)}
+    return out
+
+
 def ratio_sweep(kvq, wl, dev, cs, kv, sc, c4_pool, c4_slots, reps=5):
     """NEXT-row measurements on the resident C128A inputs (2,097,152 fp32 rows of kv and
     score): every supported ratio r >= 2 compresses the same input rows into 2,097,152 / r
@@ -459,7 +485,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-micro", action="store_true",
-                    help="skip the graph-replayed latency table and the hoisting case")
+                    help="skip the measurements beside the step: FP4 C4A/C128A, store configs, "
+                         "latency table, hoisting case, ratio sweep")
     ap.add_argument("--write-profiles", metavar="RESULTS",
                     help="summarise rocprofv3 CSVs under RESULTS into profiles/ and exit (no GPU)")
     args = ap.parse_args()
@@ -611,6 +638,12 @@ def main():
                                           f"({avg_stream_ms[n] * 1e3:.1f} between stream events)"
                                           for n in names))
 
+    fp4 = None
+    if not args.no_micro:
+        fp4 = fp4_configs(kvq, inputs, cs)
+        log(f"fp4 configs: c4a {fp4['c4a']['us']} us ({fp4['c4a']['frac_of_peak']}), "
+            f"c128a {fp4['c128a']['us']} us ({fp4['c128a']['frac_of_peak']})")
+
     # achievable-bandwidth reference (context): a plain 1 GiB device copy
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev).normal_()
     dst = torch.empty_like(src)
@@ -737,6 +770,7 @@ def main():
             "c4a_us_here": kernels["compress_c4a"]["us"], "c128a_us_here": kernels[dom]["us"],
         },
         "next_rows": nxt,
+        "fp4_configs": fp4,
         "c4a": {"rows/s": kernels["compress_c4a"]["rows/s"], "GB/s": kernels["compress_c4a"]["GB/s"],
                 "frac_of_peak": kernels["compress_c4a"]["frac_of_peak"]},
         "c128a": {"rows/s": kernels[dom]["rows/s"], "GB/s": kernels[dom]["GB/s"],
