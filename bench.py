@@ -136,8 +136,9 @@ def store_configs(kvq, wl, dev, cs, reps=20, calls=50):
               lambda: kvq.kv_store_rope(pool2, kvq.V41, k2, p2, cs, s2)))
     for name, n, b, fn in cases:
         us = graph_us(fn, calls, reps)
+        gbs = b / (us * 1e-6) / 1e9
         out[name] = {"tokens": n, "us_per_launch": round(us, 3), "tokens/s": round(n / (us * 1e-6), 1),
-                     "alg_bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1)}
+                     "alg_bytes": b, "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
     return out
 
 
