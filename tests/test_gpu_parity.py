@@ -329,7 +329,7 @@ def test_c128a_full_size_sampled(kvq, orc, cos_sin, cos_sin_dev, layout):
 
 # ------------------------------------------------------------------ decode-step state
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("ratio,S,T", [(1, 40, 5), (4, 96, 41), (128, 24, 300)])
+@pytest.mark.parametrize("ratio,S,T", [(1, 40, 5), (4, 96, 41), (7, 30, 40), (128, 24, 300), (200, 8, 450)])
 def test_compress_state_decode_steps(kvq, orc, cos_sin, cos_sin_dev, layout, ratio, S, T):
     """S sequences add one row per step (sequence s joins at step t0[s]); every completed
     window must equal the batch compressor's result on the same rows (tolerance rule),
