@@ -74,7 +74,8 @@ def test_boundary_slots_compress(kvq, orc, cs_small, layout, ratio):
     got = to_host(pool)
     valid = (EDGE_SLOTS >= 0) & (EDGE_SLOTS < NUM_PAGES * 64) & (pos >= 0) & (pos < 100)
     f64, _ = orc.pool_rows(kv, sc, ratio)
-    compare_compressed(got, ref, layout, EDGE_SLOTS[valid], f64[valid], label=f"edge slots r{ratio}")
+    compare_compressed(got, ref, layout, EDGE_SLOTS[valid], f64[valid], label=f"edge slots r{ratio}",
+                       rope=(pos[valid], cs_small))
     assert untouched_equal(got, ref, layout, EDGE_SLOTS[valid])
 
 
@@ -114,7 +115,7 @@ def test_compress_extreme_values(kvq, orc, layout, ratio):
     ref = orc.new_pool(layout, NUM_PAGES)
     orc.kv_compress_store(layout, ref, kv, sc, ratio, pos, cs, slots)
     f64, _ = orc.pool_rows(kv, sc, ratio)
-    compare_compressed(to_host(pool), ref, layout, slots, f64, label=f"extreme r{ratio} L{layout}")
+    compare_compressed(to_host(pool), ref, layout, slots, f64, label=f"extreme r{ratio} L{layout}", rope=(pos, cs))
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
@@ -146,7 +147,8 @@ def test_compress_state_edges(kvq, orc, layout):
     valid = slots < NUM_PAGES * 64
     f64, _ = orc.pool_rows(kv, sc, ratio)
     got = to_host(pool)
-    compare_compressed(got, ref, layout, slots[valid], f64[valid], label=f"state edges L{layout}")
+    compare_compressed(got, ref, layout, slots[valid], f64[valid], label=f"state edges L{layout}",
+                       rope=(pos[valid], cs))
     assert untouched_equal(got, ref, layout, slots[valid])
 
 
@@ -206,7 +208,7 @@ def test_pool_larger_than_4gib(kvq, orc, cs_small):
     orc.kv_compress_store(V41, ref2, kv, sc, 4, pos, cs_small, small_slots)
     f64, _ = orc.pool_rows(kv, sc, 4)
     got2 = to_host(pool[torch.from_numpy(pages).to("cuda")])
-    compare_compressed(got2, ref2, V41, small_slots, f64, label="pool > 4 GiB")
+    compare_compressed(got2, ref2, V41, small_slots, f64, label="pool > 4 GiB", rope=(pos, cs_small))
     del pool
     torch.cuda.empty_cache()
 
@@ -318,4 +320,4 @@ def test_compress_score_spread(kvq, orc, ratio, sigma):
     ref = orc.new_pool(V41, NUM_PAGES)
     orc.kv_compress_store(V41, ref, kv, sc, ratio, pos, cs, slots)
     f64, _ = orc.pool_rows(kv, sc, ratio)
-    compare_compressed(to_host(pool), ref, V41, slots, f64, label=f"spread {sigma} r{ratio}")
+    compare_compressed(to_host(pool), ref, V41, slots, f64, label=f"spread {sigma} r{ratio}", rope=(pos, cs))

@@ -2,7 +2,7 @@
 
 Small cases span several workgroups and a ragged tail and are compared on the whole
 pool; the full-size workloads run in the same launch configuration as the benchmark and
-are compared on sampled rows that the oracle recomputes one by one.
+are compared on every row, with the oracle run chunk by chunk as the inputs are generated.
 """
 import numpy as np
 import pytest
@@ -194,7 +194,7 @@ def test_store_norm_rope_within_tolerance(kvq, orc, cos_sin, cos_sin_dev, layout
     xv = (k.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     wv = (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     exact = xv * wv / np.sqrt((xv * xv).mean(axis=1, keepdims=True) + eps)
-    compare_compressed(got, ref, layout, slots, exact, label=f"norm n{n} L{layout}")
+    compare_compressed(got, ref, layout, slots, exact, label=f"norm n{n} L{layout}", rope=(pos, cos_sin))
     assert untouched_equal(got, ref, layout, slots)
 
 
@@ -239,7 +239,7 @@ def test_compress_small_within_tolerance(kvq, orc, cos_sin, cos_sin_dev, layout,
     log(f"[compress] ratio {ratio}, R {R}, layout {layout}")
     got, ref = run_compress(kvq, orc, layout, ratio, kv, sc, pos, slots, num_pages, cos_sin, cos_sin_dev)
     f64, _ = orc.pool_rows(kv, sc, ratio)
-    compare_compressed(got, ref, layout, slots, f64, label=f"r{ratio} R{R} L{layout}")
+    compare_compressed(got, ref, layout, slots, f64, label=f"r{ratio} R{R} L{layout}", rope=(pos, cos_sin))
     assert untouched_equal(got, ref, layout, slots)
 
 
@@ -266,65 +266,53 @@ def test_compress_skips_invalid_rows_and_honours_stride(kvq, orc, cos_sin, cos_s
     orc.kv_compress_store(layout, ref, kv, sc, ratio, pos, short, slots)
     valid = (slots >= 0) & (slots < num_pages * 64) & (pos >= 0) & (pos < 4000)
     f64, _ = orc.pool_rows(kv, sc, ratio)
-    compare_compressed(got, ref, layout, slots[valid], f64[valid], label="stride/skip")
+    compare_compressed(got, ref, layout, slots[valid], f64[valid], label="stride/skip", rope=(pos[valid], short))
     assert untouched_equal(got, ref, layout, slots[valid])
     torch.cuda.synchronize()
 
 
-def sampled_compressor_check(kvq, orc, layout, ratio, R, seed, n_sample, cos_sin, cos_sin_dev):
-    """Full-size workload on the GPU; the oracle recomputes n_sample sampled rows."""
+def full_compressor_check(kvq, orc, layout, ratio, R, seed, cos_sin, cos_sin_dev):
+    """Full-size workload, launched as the benchmark launches it; the oracle computes every
+    output row, chunk by chunk as the inputs are generated (so the whole input never sits
+    in host memory), and all R rows are compared."""
     import torch
     meta = wl.compressor_meta(seed, R)
-    log(f"[full] ratio {ratio} R {R}: generating inputs", )
+    log(f"[full] ratio {ratio} R {R}: generating inputs, oracle on every row")
     kv = torch.empty((R * ratio, 512), dtype=torch.float32, device="cuda")
     sc = torch.empty_like(kv)
-    step = max(1, (1 << 26) // (512 * ratio))      # output rows per upload chunk
+    ref = orc.new_pool(layout, meta["num_pages"])
+    f64 = np.empty((R, 512), np.float64)
+    step = max(1, (1 << 26) // (512 * ratio))      # output rows per chunk
     for i0 in range(0, R, step):
         n = min(step, R - i0)
         a, b = wl.compressor_window(seed, ratio, i0, n)
         kv[i0 * ratio:(i0 + n) * ratio].copy_(torch.from_numpy(a))
         sc[i0 * ratio:(i0 + n) * ratio].copy_(torch.from_numpy(b))
+        orc.kv_compress_store(layout, ref, a, b, ratio, np.ascontiguousarray(meta["pos"][i0:i0 + n]),
+                              cos_sin, np.ascontiguousarray(meta["slots"][i0:i0 + n]))
+        f64[i0:i0 + n] = orc.pool_rows(a, b, ratio)[0]
     pool = kvq.new_pool(layout, meta["num_pages"])
-    log(f"[full] ratio {ratio}: launching", )
+    log(f"[full] ratio {ratio}: launching")
     kvq.kv_compress_store(pool, layout, kv, sc, ratio, to_dev(meta["pos"]), cos_sin_dev,
                           to_dev(meta["slots"]))
     torch.cuda.synchronize()
     got = to_host(pool)
     del kv, sc
-    # sampled rows: runs of `blk` consecutive output rows at random places, plus the first
-    # and the last run (the oracle regenerates just those windows)
-    blk = max(1, n_sample // 16)
-    rng = np.random.default_rng(seed + 99)
-    starts = np.sort(rng.choice(R // blk, 16, replace=False)) * blk
-    starts[0], starts[-1] = 0, R - blk
-    starts = np.unique(starts)
-    pick = np.concatenate([np.arange(s, s + blk) for s in starts])
-    wins = [wl.compressor_window(seed, ratio, int(s), blk) for s in starts]
-    kvs = np.concatenate([w[0] for w in wins])
-    scs = np.concatenate([w[1] for w in wins])
-    ref = orc.new_pool(layout, meta["num_pages"])
-    slots, pos = meta["slots"][pick].copy(), meta["pos"][pick].copy()
-    orc.kv_compress_store(layout, ref, kvs, scs, ratio, pos, cos_sin, slots)
-    f64, _ = orc.pool_rows(kvs, scs, ratio)
-    compare_compressed(got, ref, layout, slots, f64, label=f"full r{ratio} L{layout}")
-    # every slot of the workload was written, nothing else
-    written = np.zeros(got.shape[0] * 64, bool)
-    written[meta["slots"]] = True
-    cr = {V41: 512, FP4: 256}[layout]
-    rows_nonzero = got[:, :64 * cr].reshape(got.shape[0], 64, cr).any(axis=2).reshape(-1)
-    assert not rows_nonzero[~written].any()
+    compare_compressed(got, ref, layout, meta["slots"], f64, label=f"full r{ratio} L{layout}",
+                       rope=(meta["pos"], cos_sin))
+    assert untouched_equal(got, ref, layout, meta["slots"])   # nothing outside the slots
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("layout", LAYOUTS)
-def test_c4a_full_size_sampled(kvq, orc, cos_sin, cos_sin_dev, layout):
-    sampled_compressor_check(kvq, orc, layout, 4, 16384, 3, 2048, cos_sin, cos_sin_dev)
+def test_c4a_full_size_every_row(kvq, orc, cos_sin, cos_sin_dev, layout):
+    full_compressor_check(kvq, orc, layout, 4, 16384, 3, cos_sin, cos_sin_dev)
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("layout", LAYOUTS)
-def test_c128a_full_size_sampled(kvq, orc, cos_sin, cos_sin_dev, layout):
-    sampled_compressor_check(kvq, orc, layout, 128, 16384, 4, 96, cos_sin, cos_sin_dev)
+def test_c128a_full_size_every_row(kvq, orc, cos_sin, cos_sin_dev, layout):
+    full_compressor_check(kvq, orc, layout, 128, 16384, 4, cos_sin, cos_sin_dev)
 
 
 # ------------------------------------------------------------------ decode-step state
@@ -367,7 +355,7 @@ def test_compress_state_decode_steps(kvq, orc, cos_sin, cos_sin_dev, layout, rat
     got = to_host(pool)
     assert np.array_equal(to_host(count)[sid_of], (nrows % ratio).astype(np.int32))
     ref = orc.new_pool(layout, num_pages)
-    done_slots, f64s = [], []
+    done_slots, done_pos, f64s = [], [], []
     for s_ in range(S):
         if nwin[s_] == 0:
             continue
@@ -377,10 +365,12 @@ def test_compress_state_decode_steps(kvq, orc, cos_sin, cos_sin_dev, layout, rat
         orc.kv_compress_store(layout, ref, kvw, scw, ratio, np.ascontiguousarray(win_pos[s_][:nwin[s_]]),
                               cos_sin, sl)
         done_slots.append(sl)
+        done_pos.append(win_pos[s_][:nwin[s_]])
         f64s.append(orc.pool_rows(kvw, scw, ratio)[0])
     done = np.concatenate(done_slots)
     log(f"[state] ratio {ratio}: {done.size} windows completed over {T} steps")
-    compare_compressed(got, ref, layout, done, np.concatenate(f64s), label=f"state r{ratio} L{layout}")
+    compare_compressed(got, ref, layout, done, np.concatenate(f64s), label=f"state r{ratio} L{layout}",
+                       rope=(np.concatenate(done_pos), cos_sin))
     assert untouched_equal(got, ref, layout, done)   # incomplete windows wrote nothing
 
 
@@ -500,6 +490,6 @@ def test_mixed_fp4_step(kvq, orc, cos_sin, cos_sin_dev):
     ref_pool = orc.new_pool(FP4, d["num_pages"])
     orc.kv_compress_store(FP4, ref_pool, d["kv"], d["score"], 4, d["pos"], cos_sin, slots)
     f64, _ = orc.pool_rows(d["kv"], d["score"], 4)
-    compare_compressed(got_pool, ref_pool, FP4, slots, f64, label="mixed fp4")
+    compare_compressed(got_pool, ref_pool, FP4, slots, f64, label="mixed fp4", rope=(d["pos"], cos_sin))
     assert untouched_equal(got_pool, ref_pool, FP4, slots)
     assert np.array_equal(to_host(ws), orc.kv_dequant(FP4, got_pool, d["page_ids"]))
