@@ -271,35 +271,38 @@ def test_compress_skips_invalid_rows_and_honours_stride(kvq, orc, cos_sin, cos_s
     torch.cuda.synchronize()
 
 
-def full_compressor_check(kvq, orc, layout, ratio, R, seed, cos_sin, cos_sin_dev):
-    """Full-size workload, launched as the benchmark launches it; the oracle computes every
-    output row, chunk by chunk as the inputs are generated (so the whole input never sits
-    in host memory), and all R rows are compared."""
+def full_compressor_check(kvq, orc, layout, ratio, R, seed, cos_sin, cos_sin_dev, num_pages=4096):
+    """Full-size workload, launched as the benchmark launches it, compared on every output
+    row.  Pass 1 generates the inputs chunk by chunk, uploads them and lets the oracle
+    write its pool; after the launch, pass 2 regenerates each chunk for the exact pooled
+    values and compares that chunk's rows, so no full-size host copy is ever held."""
     import torch
-    meta = wl.compressor_meta(seed, R)
+    meta = wl.compressor_meta(seed, R, num_pages)
     log(f"[full] ratio {ratio} R {R}: generating inputs, oracle on every row")
     kv = torch.empty((R * ratio, 512), dtype=torch.float32, device="cuda")
     sc = torch.empty_like(kv)
-    ref = orc.new_pool(layout, meta["num_pages"])
-    f64 = np.empty((R, 512), np.float64)
+    ref = orc.new_pool(layout, num_pages)
     step = max(1, (1 << 26) // (512 * ratio))      # output rows per chunk
-    for i0 in range(0, R, step):
-        n = min(step, R - i0)
+    chunks = [(i0, min(step, R - i0)) for i0 in range(0, R, step)]
+    for i0, n in chunks:
         a, b = wl.compressor_window(seed, ratio, i0, n)
         kv[i0 * ratio:(i0 + n) * ratio].copy_(torch.from_numpy(a))
         sc[i0 * ratio:(i0 + n) * ratio].copy_(torch.from_numpy(b))
         orc.kv_compress_store(layout, ref, a, b, ratio, np.ascontiguousarray(meta["pos"][i0:i0 + n]),
                               cos_sin, np.ascontiguousarray(meta["slots"][i0:i0 + n]))
-        f64[i0:i0 + n] = orc.pool_rows(a, b, ratio)[0]
-    pool = kvq.new_pool(layout, meta["num_pages"])
+    pool = kvq.new_pool(layout, num_pages)
     log(f"[full] ratio {ratio}: launching")
     kvq.kv_compress_store(pool, layout, kv, sc, ratio, to_dev(meta["pos"]), cos_sin_dev,
                           to_dev(meta["slots"]))
     torch.cuda.synchronize()
     got = to_host(pool)
-    del kv, sc
-    compare_compressed(got, ref, layout, meta["slots"], f64, label=f"full r{ratio} L{layout}",
-                       rope=(meta["pos"], cos_sin))
+    del kv, sc, pool
+    for i0, n in chunks:
+        a, b = wl.compressor_window(seed, ratio, i0, n)
+        f64 = orc.pool_rows(a, b, ratio)[0]
+        compare_compressed(got, ref, layout, meta["slots"][i0:i0 + n], f64,
+                           label=f"full r{ratio} L{layout} rows {i0}+{n}",
+                           rope=(meta["pos"][i0:i0 + n], cos_sin))
     assert untouched_equal(got, ref, layout, meta["slots"])   # nothing outside the slots
 
 
@@ -313,6 +316,16 @@ def test_c4a_full_size_every_row(kvq, orc, cos_sin, cos_sin_dev, layout):
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_c128a_full_size_every_row(kvq, orc, cos_sin, cos_sin_dev, layout):
     full_compressor_check(kvq, orc, layout, 128, 16384, 4, cos_sin, cos_sin_dev)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("ratio", [2, 8, 16, 32, 64])
+def test_ratio_sweep_size_every_row(kvq, orc, cos_sin, cos_sin_dev, ratio):
+    """The benchmark's ratio sweep shape: 2,097,152 input rows (8 GiB of kv and score)
+    compressed at each ratio, V41, every output row compared."""
+    R = 2097152 // ratio
+    full_compressor_check(kvq, orc, V41, ratio, R, 40 + ratio, cos_sin, cos_sin_dev,
+                          num_pages=max(4096, (R * 5 // 4) // 64 + 1))
 
 
 # ------------------------------------------------------------------ decode-step state
