@@ -506,3 +506,32 @@ def test_mixed_fp4_step(kvq, orc, cos_sin, cos_sin_dev):
     compare_compressed(got_pool, ref_pool, FP4, slots, f64, label="mixed fp4", rope=(d["pos"], cos_sin))
     assert untouched_equal(got_pool, ref_pool, FP4, slots)
     assert np.array_equal(to_host(ws), orc.kv_dequant(FP4, got_pool, d["page_ids"]))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_compress_state_bench_shape(kvq, orc, cos_sin, cos_sin_dev, layout):
+    """The benchmark's decode shape: 16,384 sequences, ratio 4, one row per sequence per
+    call in a shuffled order, one full window each; every window compared."""
+    import torch
+    S, ratio, num_pages = 16384, 4, 4096
+    rng = np.random.default_rng(77)
+    kv = rng.standard_normal((S * ratio, 512)).astype(np.float32)     # window of s: rows [4s, 4s+4)
+    sc = (2 * rng.standard_normal((S * ratio, 512))).astype(np.float32)
+    pos = rng.integers(0, 65536, S).astype(np.int32)
+    slots = wl.distinct_slots(rng, S, 64, num_pages * 64)
+    pool = kvq.new_pool(layout, num_pages)
+    state, count = kvq.new_compress_state(S)
+    for t in range(ratio):
+        order = rng.permutation(S).astype(np.int32)
+        rows = order * ratio + t
+        kvq.kv_compress_state_update(pool, layout, state, count, ratio, to_dev(order), to_dev(kv[rows]),
+                                     to_dev(sc[rows]), to_dev(pos[order]), cos_sin_dev, to_dev(slots[order]))
+    torch.cuda.synchronize()
+    assert not to_host(count).any()
+    ref = orc.new_pool(layout, num_pages)
+    orc.kv_compress_store(layout, ref, kv, sc, ratio, pos, cos_sin, slots)
+    got = to_host(pool)
+    compare_compressed(got, ref, layout, slots, orc.pool_rows(kv, sc, ratio)[0],
+                       label=f"state bench shape L{layout}", rope=(pos, cos_sin))
+    assert untouched_equal(got, ref, layout, slots)
