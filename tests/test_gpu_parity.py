@@ -178,7 +178,7 @@ def test_store_rope_edges(kvq, orc, cos_sin, cos_sin_dev, layout):
 
 # ------------------------------------------------------------------ K norm + RoPE
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("n,eps", [(1, 1e-6), (130, 1e-6), (512, 0.0), (1001, 0.25)])
+@pytest.mark.parametrize("n,eps", [(1, 1e-6), (130, 1e-6), (512, 0.0), (1001, 0.25), (65536, 1e-6)])
 def test_store_norm_rope_within_tolerance(kvq, orc, cos_sin, cos_sin_dev, layout, n, eps):
     import torch
     rng = np.random.default_rng(200 + n)
