@@ -352,6 +352,8 @@ PROFILE_RUNS = {
              "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-micro",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d $RESULTS/pmc_write -o write -- "
              "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-micro",
+    "next": "rocprofv3 --kernel-trace --stats -f csv -d $RESULTS/prof_next -o next -- "
+            "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
 }
 SHORT_NAMES = {
     "compress_long_kernel<(kvq::Layout)1, 128": "compress_long<V41, ratio 128> (C128A)",
@@ -469,11 +471,62 @@ def pmc_summary(results):
     return "\n".join(lines) + "\n"
 
 
+def _kernel_label(name):
+    """Readable label of a library kernel from its (demangled) name, e.g.
+    compress_long_kernel<V41, 64, 8, 2>; None for kernels outside the library."""
+    import re
+    m = re.search(r"kvq::(\w+)(?:<([^>]*)>)?\(", name)
+    if m is None:
+        return None
+    args = m.group(2)
+    if args:
+        args = args.replace("(kvq::Layout)1", "V41").replace("(kvq::Layout)2", "V41_FP4")
+        return f"{m.group(1)}<{args}>"
+    return m.group(1)
+
+
+def all_kernels_summary(results):
+    """Every library kernel of the run that includes the measurements beside the step,
+    grouped by kernel and grid (one line per configuration), with its registers and LDS."""
+    import csv
+    import numpy as np
+    groups = {}
+    for r in csv.DictReader(open(_find_csv(results, "prof_next/**/next_kernel_trace.csv"))):
+        label = _kernel_label(r["Kernel_Name"])
+        if label is None:
+            continue
+        wg = int(r["Workgroup_Size_X"])
+        key = (label, int(r["Grid_Size_X"]) // wg, wg, int(r["LDS_Block_Size"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [
+        "# rocprofv3 kernel-trace summary: every library kernel of one full bench run (one timed",
+        "# step plus the measurements beside it: FP4 C4A/C128A, store configs, graph-replayed",
+        "# latency table, hoisting case, ratio sweep, token gather, decode state), MI355X,",
+        "# one line per kernel and grid (workgroups x threads per workgroup), with the LDS bytes",
+        "# per workgroup the trace reports",
+        f"# command: {PROFILE_RUNS['next']}",
+        "# (run from the repository root with TMPDIR=/tmp, RESULTS = the results directory;",
+        "#  summarised by: python bench.py --write-profiles $RESULTS)",
+        "",
+        f"{'kernel':<44} {'workgroups':>10} {'thr':>5} {'lds':>6} {'calls':>6} "
+        f"{'avg_us':>9} {'min_us':>9} {'max_us':>9}",
+    ]
+    for (label, nwg, wg, lds), t in sorted(groups.items()):
+        t = np.array(t)
+        lines.append(f"{label:<44} {nwg:>10} {wg:>5} {lds:>6} {t.size:>6} "
+                     f"{t.mean():>9.2f} {t.min():>9.2f} {t.max():>9.2f}")
+    return "\n".join(lines) + "\n"
+
+
 def write_profiles(results):
     out = os.path.join(ROOT, "profiles")
     os.makedirs(out, exist_ok=True)
-    for name, text in (("bench_step_kernel_trace.txt", trace_summary(results)),
-                       ("compress_c128a_v41_pmc.txt", pmc_summary(results))):
+    outputs = [("bench_step_kernel_trace.txt", trace_summary(results)),
+               ("compress_c128a_v41_pmc.txt", pmc_summary(results))]
+    import glob
+    if glob.glob(os.path.join(results, "prof_next/**/next_kernel_trace.csv"), recursive=True):
+        outputs.append(("all_kernels_full_bench_trace.txt", all_kernels_summary(results)))
+    for name, text in outputs:
         with open(os.path.join(out, name), "w") as fh:
             fh.write(text)
         print(text)

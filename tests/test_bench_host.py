@@ -66,3 +66,19 @@ def test_pmc_summary_scales_by_the_copy_and_round_trips(results, tmp_path, monke
     prof.write_text(text.replace(bench.kernel_source_hash(), "0" * 64))
     assert bench.read_traffic(bench.bytes_compress(16384, 128, 528)) is None
 
+
+
+def test_all_kernels_summary_groups_by_kernel_and_grid(tmp_path):
+    hdr = ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp", "LDS_Block_Size",
+           "Workgroup_Size_X", "Grid_Size_X"]
+    short4 = "void kvq::compress_short_kernel<(kvq::Layout)1, 4>(unsigned char*, long)"
+    rows = [["KERNEL_DISPATCH", short4, 0, 47000, 0, 256, 4096 * 256],
+            ["KERNEL_DISPATCH", short4, 0, 45000, 0, 256, 4096 * 256],
+            ["KERNEL_DISPATCH", short4, 0, 1620000, 0, 256, 131072 * 256],
+            ["KERNEL_DISPATCH", "__amd_rocclr_copyBuffer", 0, 5, 0, 256, 256]]
+    _write(str(tmp_path / "prof_next" / "next_kernel_trace.csv"), hdr, rows)
+    text = bench.all_kernels_summary(str(tmp_path))
+    lines = [ln for ln in text.splitlines() if ln.startswith("compress_short_kernel<V41, 4>")]
+    assert len(lines) == 2                                   # one line per grid
+    assert lines[0].split()[2:6] == ["4096", "256", "0", "2"] and "46.00" in lines[0]
+    assert "copyBuffer" not in text
