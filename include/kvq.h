@@ -33,9 +33,12 @@
  *    call are a caller error (which row wins is unspecified).
  *  - n == 0 (or R == 0, P == 0) returns KVQ_OK without launching, except
  *    kv_translate_slots, which still zeroes out[0:cap].
- *  - Inputs must be finite, with |kv| * ratio and |score| * 1.5 below FLT_MAX (the fp32
- *    pooling sums at most `ratio` weighted rows and scales scores by log2(e));
- *    values outside that domain give unspecified codes.  fp32 denormals are handled.
+ *  - Sizes above what one launch covers are refused with KVQ_EINVAL before anything is
+ *    enqueued: rows n (or R) <= KVQ_MAX_ROWS, except R <= KVQ_MAX_LONG_ROWS for
+ *    compressor ratios of 8 and more; pages P <= KVQ_MAX_PAGES; cap <= 2^31 - 1.
+ *  - Inputs must be finite, with |kv| no larger than the largest finite bf16
+ *    (about 3.39e38) so that no pooled value rounds to infinity; values outside that
+ *    domain give unspecified codes.  fp32 denormals are handled.
  *
  * Pool layout (PagedKV, page size 64 tokens, [P1] section 1): the pool is num_pages
  * pages of kvq_page_bytes(layout) bytes each, contiguous from `pool`.  Slot s lives in
@@ -74,6 +77,11 @@ extern "C" {
 #define KVQ_ECAPACITY (-4) /* kv_translate_slots with n > cap; nothing enqueued   */
 #define KVQ_ELAUNCH (-5)   /* the HIP runtime rejected the kernel launch          */
 
+/* ---- size limits of one call (larger requests return KVQ_EINVAL) --------------- */
+#define KVQ_MAX_ROWS 33554432      /* 2^25 rows of a store / gather / short-window call */
+#define KVQ_MAX_LONG_ROWS 4194304  /* 2^22 output rows of a compressor call, ratio >= 8 */
+#define KVQ_MAX_PAGES 524288       /* 2^19 page ids of one kv_dequant call              */
+
 /* ---- layout ids ---------------------------------------------------------------- */
 #define KVQ_LAYOUT_V41 1     /* fp8 e4m3 codes + ue8m0 scale per 32: 528 B/token     */
 #define KVQ_LAYOUT_V41_FP4 2 /* e2m1 codes + e4m3 scale per 32 (+pad): 288 B/token  */
@@ -90,6 +98,11 @@ int kvq_profile_next_launch(void* start_event, void* stop_event);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* kvq_status_string(int status);
+
+/* Identity of the build: the SHA-256 (hex) of the kernel sources this library was
+ * compiled from (static string).  Loaders compare it with the sources next to them to
+ * refuse a stale library. */
+const char* kvq_build_id(void);
 
 /* Layout queries ([P1] sections 1 and 5).  Each returns the byte count, or
  * KVQ_ELAYOUT for an unknown layout. */
@@ -123,13 +136,13 @@ int kv_store_rope(int32_t layout, void* pool, int64_t num_pages, const uint16_t*
 
 /* kv_store_norm_rope -- the fused "K norm + RoPE" store of [P1]'s latency table.  The
  * page gives no formula; this library reads it as RMS normalisation of the whole row with
- * a per-channel weight, y_c = bf16(x_c * w_c / sqrt(mean_c(x_c^2) + eps)) (computed in
- * fp32), followed by kv_store_rope on y.
+ * a per-channel weight, y_c = bf16((x_c * w_c) / sqrt(mean_c(x_c^2) + eps)), evaluated in
+ * float64 (x_c * w_c and the squares exact, the mean a float64 sum, IEEE sqrt and
+ * division) and rounded once to bf16, followed by kv_store_rope on y.
  *   weight     device bf16 bits [512], 16-byte aligned
  *   eps        >= 0 and finite (else KVQ_EINVAL)
- * Other arguments as kv_store_rope.  y may differ from an exact (float64) evaluation by
- * one bf16 step where the fp32 result rounds the other way, so codes may differ by at
- * most one step from such an evaluation. */
+ * Other arguments as kv_store_rope.  y equals the correctly rounded value unless the
+ * exact quotient lies within a few float64 ulps of a bf16 rounding midpoint. */
 int kv_store_norm_rope(int32_t layout, void* pool, int64_t num_pages, const uint16_t* k,
                        int64_t ld, const uint16_t* weight, float eps, const int32_t* pos,
                        const float* cos_sin, int64_t max_pos, const int32_t* slots, int64_t n,
@@ -138,19 +151,24 @@ int kv_store_norm_rope(int32_t layout, void* pool, int64_t num_pages, const uint
 /* kv_compress_store -- the c1 / C4A / C128A compressors ([P3] sections 1-3; [P1]
  * section 2).  Output row i pools input rows [i*ratio, i*ratio + ratio) channel by
  * channel: weights are the softmax over the window of score[.][c], the pooled value is
- * the weighted sum of kv[.][c] (computed in fp32 with an online max, then rounded to
- * bf16); then RoPE at pos[i] as in kv_store_rope; then quantise and store at slots[i].
- * ratio 1 is the identity (score is not read).
+ * the weighted sum of kv[.][c], evaluated in float64 (weights exp(s - ref) against a
+ * reference score of the window, online over the window) and rounded once to bf16; then
+ * RoPE at pos[i] as in kv_store_rope; then quantise and store at slots[i].  ratio 1 is
+ * the identity (score is not read).
  *   kv, score  device fp32, row j at base + j*ld, R*ratio rows; 16-byte aligned
  *   ld         row stride in elements, >= 512 and a multiple of 4
  *   ratio      1, 2, 4, 8, 16, 32, 64 or 128 (others: KVQ_ERATIO)
  *   pos, slots device int32[R]
- * Compressed codes may differ from an exact (float64) evaluation by at most one code
- * step where the fp32 pooled value rounds to a different bf16. */
+ * The pooled bf16 equals the correctly rounded exact value unless that value lies within
+ * about 1e-15 (relative to the window's |kv|) of a bf16 rounding midpoint; every later
+ * step is exact, so the stored bytes are then those of the exact evaluation. */
 int kv_compress_store(int32_t layout, void* pool, int64_t num_pages, const float* kv,
                       const float* score, int64_t ld, int32_t ratio, const int32_t* pos,
                       const float* cos_sin, int64_t max_pos, const int32_t* slots,
                       int64_t R, void* stream);
+
+/* Bytes of one sequence's decode-step compressor state (kv_compress_state_update). */
+int64_t kvq_compress_state_bytes(void);  /* 10240 */
 
 /* kv_compress_state_update -- the compressor across decode steps: windows that fill one
  * row per step are folded into a per-sequence online-softmax state instead of keeping
@@ -162,15 +180,17 @@ int kv_compress_store(int32_t layout, void* pool, int64_t num_pages, const float
  * stores nothing) and the state becomes empty again.  Rows of one window must arrive in
  * order, at most one row per state per call (state_ids distinct within a call; repeats
  * race).  A state id outside [0, num_states) skips the row.
- *   state      device fp32 [num_states][3][512], contents opaque; 16-byte aligned
+ *   state      device, num_states * kvq_compress_state_bytes() bytes, contents opaque
+ *              (a float64 online-softmax state per sequence); 16-byte aligned
  *   count      device int32 [num_states]: rows folded so far; 0 = empty.  A zeroed
  *              state + count is a valid starting point.
  *   ratio      window length, 1 .. 2^20
  *   pos, slots device int32[n]: used for the row that completes its window
  *   kv, score  device fp32 rows, row j at base + j*ld; 16-byte aligned, ld >= 512, % 4
- * The finalised row may differ from kv_compress_store on the same window by at most one
- * code step (the fold runs in a different fp32 order). */
-int kv_compress_state_update(int32_t layout, void* pool, int64_t num_pages, float* state,
+ * The fold is float64 like kv_compress_store's, so a finalised row carries the same
+ * bytes as kv_compress_store on the same window (up to the float64 evaluation order,
+ * which matters only within about 1e-15 of a bf16 rounding midpoint). */
+int kv_compress_state_update(int32_t layout, void* pool, int64_t num_pages, void* state,
                              int32_t* count, int64_t num_states, int32_t ratio,
                              const int32_t* state_ids, const float* kv, const float* score,
                              int64_t ld, const int32_t* pos, const float* cos_sin,

@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "V41", "V41_FP4", "KVQError", "load_library", "profile_next_launch", "bytes_per_token", "page_bytes",
     "code_row_bytes", "scale_row_bytes", "new_pool", "kv_store", "kv_store_rope", "kv_store_norm_rope",
-    "kv_compress_store", "kv_compress_state_update", "new_compress_state", "kv_dequant", "kv_dequant_slots", "kv_translate_slots", "SUPPORTED_RATIOS",
+    "kv_compress_store", "kv_compress_state_update", "new_compress_state", "compress_state_bytes", "kv_dequant", "kv_dequant_slots", "kv_translate_slots", "SUPPORTED_RATIOS",
 ]
 
 V41 = 1
@@ -39,17 +39,27 @@ class KVQError(RuntimeError):
 
 
 def load_library() -> ctypes.CDLL:
-    """Load libkvq.so; raises if it has not been built."""
+    """Load libkvq.so; raises if it has not been built, or if it was built from other
+    sources than the ones next to it (its kvq_build_id differs from their hash)."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python -m quantized_paged_kv_compress_amd._build`")
+    from . import _build
     L = ctypes.CDLL(LIB_PATH)
+    L.kvq_build_id.restype = ctypes.c_char_p
+    L.kvq_build_id.argtypes = []
+    built, want = L.kvq_build_id().decode(), _build.source_hash()
+    if built != want:
+        raise ImportError(f"{LIB_PATH} is stale (built from sources {built[:12]}, current {want[:12]}): "
+                          "rebuild it with `python -m quantized_paged_kv_compress_amd._build`")
     i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
     L.kvq_status_string.restype = ctypes.c_char_p
     L.kvq_status_string.argtypes = [ctypes.c_int]
+    L.kvq_compress_state_bytes.restype = i64
+    L.kvq_compress_state_bytes.argtypes = []
     L.kvq_profile_next_launch.restype = ctypes.c_int
     L.kvq_profile_next_launch.argtypes = [vp, vp]
     for q in ("kvq_bytes_per_token", "kvq_page_bytes", "kvq_code_row_bytes", "kvq_scale_row_bytes"):
@@ -232,9 +242,15 @@ def kv_compress_store(pool, layout, kv, score, ratio, pos, cos_sin, slots, strea
         _ptr(cos_sin), cos_sin.shape[0], _ptr(slots), R, _stream(stream)))
 
 
+def compress_state_bytes() -> int:
+    """Bytes of one sequence's decode-step compressor state."""
+    return int(load_library().kvq_compress_state_bytes())
+
+
 def new_compress_state(num_states: int, device="cuda"):
-    """An empty decode-step compressor state: (fp32 [num_states, 3, 512], int32 counts)."""
-    return (torch.zeros((num_states, 3, HEAD_DIM), dtype=torch.float32, device=device),
+    """An empty decode-step compressor state: (uint8 [num_states, compress_state_bytes()]
+    opaque states, int32 counts)."""
+    return (torch.zeros((num_states, compress_state_bytes()), dtype=torch.uint8, device=device),
             torch.zeros(num_states, dtype=torch.int32, device=device))
 
 
@@ -243,10 +259,10 @@ def kv_compress_state_update(pool, layout, state, count, ratio, state_ids, kv, s
     """Fold row j of kv/score into state state_ids[j]; a window completed by row j is
     stored at slots[j] with RoPE at pos[j].  At most one row per state per call."""
     num_pages = _pool(pool, layout)
-    _dev(state, "state", _F32)
+    _dev(state, "state", (torch.uint8,))
     _vec(count, "count")
-    if not state.is_contiguous() or state.dim() != 3 or tuple(state.shape[1:]) != (3, HEAD_DIM):
-        raise ValueError("state: need a contiguous fp32 [num_states, 3, 512] tensor")
+    if not state.is_contiguous() or state.dim() != 2 or state.shape[1] != compress_state_bytes():
+        raise ValueError("state: need a contiguous uint8 [num_states, compress_state_bytes()] tensor")
     if count.numel() != state.shape[0]:
         raise ValueError("count: one int32 per state")
     ld = _rows(_dev(kv, "kv", _F32), "kv")

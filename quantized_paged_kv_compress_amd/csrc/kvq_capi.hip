@@ -18,8 +18,17 @@ namespace {
 
 using kvq::Layout;
 
-constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+// Largest request of one call: each kernel's grid must stay below 2^32 work-items in x
+// (64 per row for the row kernels, 512 per output row for the long-window compressor,
+// 64 per row of each listed page for the page dequant).
+constexpr int64_t kMaxRows = KVQ_MAX_ROWS;
+constexpr int64_t kMaxLongRows = KVQ_MAX_LONG_ROWS;
+constexpr int64_t kMaxDequantPages = KVQ_MAX_PAGES;
+constexpr int64_t kMaxCap = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxPages = int64_t(1) << 32;  // far beyond any pool; keeps num_pages * 64 exact
+static_assert(kMaxRows * 64 < (int64_t(1) << 32) && kMaxLongRows * 512 < (int64_t(1) << 32) &&
+                  kMaxDequantPages * 64 * 64 < (int64_t(1) << 32),
+              "every grid stays below 2^32 work-items");
 constexpr int64_t kDequantLongList = 1024;  // pages; from here on 4 rows per wavefront
 constexpr int32_t kMaxStateRatio = 1 << 20;
 
@@ -111,6 +120,10 @@ int compress_dispatch(int32_t ratio, void* pool, int64_t num_pages, const float*
 }  // namespace
 
 extern "C" {
+
+const char* kvq_build_id(void) { return KVQ_BUILD_ID; }
+
+int64_t kvq_compress_state_bytes(void) { return kvq::kStateBytes; }
 
 int kvq_profile_next_launch(void* start_event, void* stop_event) {
     t_start_event = static_cast<hipEvent_t>(start_event);
@@ -204,7 +217,9 @@ int kv_compress_store(int32_t layout, void* pool, int64_t num_pages, const float
     if (ratio != 1 && ratio != 2 && ratio != 4 && ratio != 8 && ratio != 16 && ratio != 32 &&
         ratio != 64 && ratio != 128)
         return KVQ_ERATIO;
-    if (R < 0 || R > kMaxRows || num_pages < 0 || num_pages > kMaxPages || max_pos <= 0) return KVQ_EINVAL;
+    if (R < 0 || R > (ratio >= 8 ? kMaxLongRows : kMaxRows) || num_pages < 0 || num_pages > kMaxPages ||
+        max_pos <= 0)
+        return KVQ_EINVAL;
     if (R == 0) return KVQ_OK;
     if (!pool || !kv || (ratio > 1 && !score) || !pos || !cos_sin || !slots) return KVQ_EINVAL;
     if (ld < kvq::kHeadDim || ld % 4 != 0) return KVQ_EINVAL;
@@ -215,7 +230,7 @@ int kv_compress_store(int32_t layout, void* pool, int64_t num_pages, const float
     return compress_dispatch<Layout::V41_FP4>(ratio, pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
 }
 
-int kv_compress_state_update(int32_t layout, void* pool, int64_t num_pages, float* state, int32_t* count,
+int kv_compress_state_update(int32_t layout, void* pool, int64_t num_pages, void* state, int32_t* count,
                              int64_t num_states, int32_t ratio, const int32_t* state_ids, const float* kv,
                              const float* score, int64_t ld, const int32_t* pos, const float* cos_sin,
                              int64_t max_pos, const int32_t* slots, int64_t n, void* stream) {
@@ -230,18 +245,19 @@ int kv_compress_state_update(int32_t layout, void* pool, int64_t num_pages, floa
         return KVQ_EINVAL;
     const dim3 grid(blocks_for(n, kvq::kRowsPerBlock)), block(kvq::kWave * kvq::kRowsPerBlock);
     auto* p = static_cast<uint8_t*>(pool);
+    auto* st = static_cast<uint8_t*>(state);
     const int64_t nslots = num_pages << kvq::kPageBits;
     if (layout == KVQ_LAYOUT_V41)
-        return launch(kvq::compress_state_kernel<Layout::V41>, grid, block, stream, p, nslots, state, count,
+        return launch(kvq::compress_state_kernel<Layout::V41>, grid, block, stream, p, nslots, st, count,
                       num_states, ratio, state_ids, kv, score, ld, pos, cos_sin, max_pos, slots, n);
-    return launch(kvq::compress_state_kernel<Layout::V41_FP4>, grid, block, stream, p, nslots, state, count,
+    return launch(kvq::compress_state_kernel<Layout::V41_FP4>, grid, block, stream, p, nslots, st, count,
                   num_states, ratio, state_ids, kv, score, ld, pos, cos_sin, max_pos, slots, n);
 }
 
 int kv_dequant(int32_t layout, const void* pool, int64_t num_pages, const int32_t* page_ids,
                int64_t P, uint16_t* out, void* stream) {
     if (!known_layout(layout)) return KVQ_ELAYOUT;
-    if (P < 0 || P > (kMaxRows >> kvq::kPageBits) || num_pages < 0 || num_pages > kMaxPages) return KVQ_EINVAL;
+    if (P < 0 || P > kMaxDequantPages || num_pages < 0 || num_pages > kMaxPages) return KVQ_EINVAL;
     if (P == 0) return KVQ_OK;
     if (!pool || !page_ids || !out) return KVQ_EINVAL;
     if (!aligned16(pool) || !aligned16(out)) return KVQ_EINVAL;
@@ -277,7 +293,7 @@ int kv_dequant_slots(int32_t layout, const void* pool, int64_t num_pages, const 
 
 int kv_translate_slots(const int32_t* table, int64_t table_len, const int32_t* full_loc, int64_t n,
                        int32_t* out, int64_t cap, void* stream) {
-    if (n < 0 || cap < 0 || table_len < 0 || cap > kMaxRows) return KVQ_EINVAL;
+    if (n < 0 || cap < 0 || table_len < 0 || cap > kMaxCap) return KVQ_EINVAL;
     if (n > cap) return KVQ_ECAPACITY;
     if (cap == 0) return KVQ_OK;
     if (!out || (n > 0 && (!table || !full_loc))) return KVQ_EINVAL;

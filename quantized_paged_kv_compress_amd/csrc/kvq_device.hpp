@@ -38,6 +38,50 @@ __device__ __forceinline__ float round_bf16(float f) {
     return __uint_as_float(bf16_rne_bits(f) << 16);
 }
 
+// float64 -> nearest bfloat16 bit pattern (ties to even), rounded once from the float64
+// value: going through float32 first could land exactly on a bf16 midpoint and round
+// twice.  At or above 2^-126 the 45 low mantissa bits are rounded away in the integer
+// domain (a carry moves into the exponent, and past the bf16 range the float32
+// conversion gives infinity); below it the bf16 spacing is the fixed 2^-133.
+__device__ __forceinline__ uint32_t bf16_rne_bits_f64(double p) {
+    const uint64_t u = static_cast<uint64_t>(__double_as_longlong(p));
+    if ((u & 0x7FFFFFFFFFFFFFFFull) < 0x3810000000000000ull) {
+        const double q = __builtin_rint(p * 0x1p133) * 0x1p-133;
+        return __float_as_uint(static_cast<float>(q)) >> 16;
+    }
+    const uint64_t r = (u + 0x00000FFFFFFFFFFFull + ((u >> 45) & 1u)) & ~0x00001FFFFFFFFFFFull;
+    return __float_as_uint(static_cast<float>(__longlong_as_double(static_cast<long long>(r)))) >> 16;
+}
+
+// ---------------------------------------------------------------- float64 exponential
+// exp(d) for float64 d up to 700, written out for the softmax weights.  k = rint(d / ln 2)
+// comes from the low bits of d / ln 2 + 1.5 * 2^52 (one fma, ties to even); r = d - k ln 2
+// is reduced in two steps with ln 2 split so that k * kLn2Hi is exact (Cody and Waite), and
+// exp(r) on |r| <= 0.35 is a degree-11 polynomial (the Chebyshev interpolant of exp on
+// [-0.35, 0.35], relative error 7e-18 before rounding; constants from gen_exp_poly.py).
+// d is held at -1000 first: exp(-1000) is already 0 in float64 and k stays small.
+// The constants sit in constant memory so that they are loaded once into scalar registers
+// and feed v_fma_f64 directly (as literals each would cost two moves per use).
+__constant__ double kExpConst[16] = {
+    0x1.af682e715258ap-26, 0x1.28b82404fa64fp-22, 0x1.71ddf2b060bb0p-19, 0x1.a0198d2d43afbp-16,
+    0x1.a01a01b24ec34p-13, 0x1.6c16c189ae5d5p-10, 0x1.111111110ef9cp-7,  0x1.555555554e892p-5,
+    0x1.555555555555bp-3,  0x1.0000000000012p-1,  1.0,                   1.0,
+    1.4426950408889634,    0x1.62e42fee00000p-1,  0x1.a39ef35793c76p-33, 0x1.8p52};
+
+__device__ __forceinline__ double exp_f64(double d) {
+    const double kInvLn2 = kExpConst[12], kLn2Hi = kExpConst[13], kLn2Lo = kExpConst[14];
+    const double kShift = kExpConst[15];
+    d = __builtin_fmax(d, -1000.0);
+    const double kd = __builtin_fma(d, kInvLn2, kShift);
+    const double k = kd - kShift;
+    double r = __builtin_fma(-k, kLn2Hi, d);
+    r = __builtin_fma(-k, kLn2Lo, r);
+    double p = kExpConst[0];
+#pragma unroll
+    for (int j = 1; j < 12; ++j) p = __builtin_fma(p, r, kExpConst[j]);
+    return __builtin_ldexp(p, static_cast<int>(__double_as_longlong(kd)));  // low word of kd = k
+}
+
 // ---------------------------------------------------------------- cross-lane
 template <int kCtrl>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
@@ -146,35 +190,126 @@ __device__ __forceinline__ void rope_apply(float (&v)[8], const RopeCS& cs, int 
     }
 }
 
+// ---------------------------------------------------------------- float64 softmax pooling
+// Online per-channel softmax pooling of a lane's 8 channels, in float64 so that the pooled
+// value rounds to the same bf16 as the exact one (an error near 1e-16 relative can only
+// change the rounding of a value that far from a bf16 midpoint).  The weights are taken
+// relative to a reference score `ref` that is a score of the window (so the largest weight
+// is at least 1): l = sum of exp(s - ref), acc = sum of exp(s - ref) * x.  The reference
+// moves, and the sums are rescaled, only when a score exceeds it by more than kRefSlack,
+// so states that start from the same reference (the window's first row) usually still
+// share it at the end and merge by plain addition.  Weights stay below e^kRefSlack.
+constexpr float kRefSlack = 64.0f;
+
+struct PoolF64 {
+    double ref[8];
+    float ref_hi[8];  // ref + kRefSlack
+    double l[8], acc[8];
+};
+
+__device__ __forceinline__ void pool_init(PoolF64& st, const float (&ref)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        st.ref[e] = ref[e];
+        st.ref_hi[e] = ref[e] + kRefSlack;
+        st.l[e] = 0.0;
+        st.acc[e] = 0.0;
+    }
+}
+
+// Fold kRows window rows (this lane's 8 kv and score values of each) into the state.
+template <int kRows>
+__device__ __forceinline__ void pool_fold(PoolF64& st, const float (&x)[kRows][8], const float (&s)[kRows][8]) {
+    float cm[8];
+    bool move = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        cm[e] = s[0][e];
+#pragma unroll
+        for (int j = 1; j < kRows; ++j) cm[e] = fmaxf(cm[e], s[j][e]);
+        move |= cm[e] > st.ref_hi[e];
+    }
+    if (move) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (cm[e] > st.ref_hi[e]) {
+                const double a = exp_f64(st.ref[e] - static_cast<double>(cm[e]));
+                st.l[e] *= a;
+                st.acc[e] *= a;
+                st.ref[e] = cm[e];
+                st.ref_hi[e] = cm[e] + kRefSlack;
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+        for (int j = 0; j < kRows; ++j) {
+            const double w = exp_f64(static_cast<double>(s[j][e]) - st.ref[e]);
+            st.l[e] += w;
+            st.acc[e] = __builtin_fma(w, static_cast<double>(x[j][e]), st.acc[e]);
+        }
+    }
+}
+
+// Bring a partial state (ref, l, acc of one channel) to the reference M >= ref.
+__device__ __forceinline__ void pool_rebase(double ref, double M, double& l, double& acc) {
+    if (ref != M) {
+        const double a = exp_f64(ref - M);
+        l *= a;
+        acc *= a;
+    }
+}
+
+// The pooled value acc / l (IEEE float64 division) as a bf16-valued float.
+__device__ __forceinline__ float pool_result(double l, double acc) {
+    return __uint_as_float(bf16_rne_bits_f64(acc / l) << 16);
+}
+
 // ---------------------------------------------------------------- K norm (RMS)
-// Sum of a float over the whole wavefront, in a fixed order: quad, pairs of quads and
-// the 16-lane DPP row by DPP adds, then the four rows through readlane.  Every lane gets
-// the same value.
-__device__ __forceinline__ float wave_sum(float v) {
-    v += __uint_as_float(dpp<0xB1>(__float_as_uint(v)));
-    v += __uint_as_float(dpp<0x4E>(__float_as_uint(v)));
-    v += __uint_as_float(dpp<0x124>(__float_as_uint(v)));   // row_ror:4
-    v += __uint_as_float(dpp<0x128>(__float_as_uint(v)));   // row_ror:8
-    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return (a + b) + (c + d);
+// One float64 DPP step of a wave reduction (the two 32-bit halves move separately).
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint64_t lo = dpp<kCtrl>(static_cast<uint32_t>(b));
+    const uint64_t hi = dpp<kCtrl>(static_cast<uint32_t>(b >> 32));
+    return __longlong_as_double(static_cast<long long>((hi << 32) | lo));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b), lane));
+    const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b >> 32), lane));
+    return __longlong_as_double(static_cast<long long>((hi << 32) | lo));
+}
+
+// Sum of a float64 over the whole wavefront in a fixed order: quad, pairs of quads and the
+// 16-lane DPP row by DPP adds, then the four rows through readlane.  Every lane gets the
+// same value.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v += dpp_f64<0xB1>(v);
+    v += dpp_f64<0x4E>(v);
+    v += dpp_f64<0x124>(v);   // row_ror:4
+    v += dpp_f64<0x128>(v);   // row_ror:8
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
 // RMS normalisation of a row with a per-channel bf16 weight (the "fused K norm + RoPE"
 // store of the sglang V41 page's latency table, read as y = x * w / sqrt(mean(x^2) + eps)),
-// in float32, results rounded to bf16.  Every lane must call this.
+// in float64: the squares and the products x * w are exact, the sum of squares is a
+// wave-wide float64 sum, 1 / sqrt(...) is IEEE float64, and each y is rounded once to
+// bf16.  Every lane must call this.
 __device__ __forceinline__ void rms_norm_row(float (&v)[8], const uint16_t* __restrict__ weight, float eps,
                                              int lane) {
     float w[8];
     load_row_bf16(weight, lane, w);
-    float ss = 0.0f;
+    double ss = 0.0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(v[e], v[e], ss);
-    const float r = 1.0f / __builtin_sqrtf(wave_sum(ss) * (1.0f / kHeadDim) + eps);
+    for (int e = 0; e < 8; ++e) ss = __builtin_fma(static_cast<double>(v[e]), static_cast<double>(v[e]), ss);
+    const double r = 1.0 / __builtin_sqrt(wave_sum_f64(ss) / kHeadDim + static_cast<double>(eps));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = round_bf16((v[e] * r) * w[e]);
+    for (int e = 0; e < 8; ++e)
+        v[e] = __uint_as_float(bf16_rne_bits_f64((static_cast<double>(v[e]) * static_cast<double>(w[e])) * r) << 16);
 }
 
 // ---------------------------------------------------------------- quantise + store

@@ -50,9 +50,10 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void store_kernel(
 // ------------------------------------------------------------------ short-window compressor
 // Ratio r <= 4: one wavefront per output row; the r window rows of kv and score are all
 // loaded up front (4r 16-byte loads per lane in flight), so the per-channel maximum is
-// exact and needs no online rescaling.  The loads and the cos/sin gather are issued
-// before the slot / position checks (which only gate the stores), so a wavefront waits
-// on memory once.  Ratio 1 is the identity and skips the scores.
+// exact and the weights exp(s - max) need no online rescaling.  The loads and the cos/sin
+// gather are issued before the slot / position checks (which only gate the stores), so a
+// wavefront waits on memory once.  Pooling is float64 (pool_* in kvq_device.hpp); ratio 1
+// is the identity and skips the scores.
 template <Layout L, int kRatio>
 __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_short_kernel(
     uint8_t* __restrict__ pool, int64_t nslots, const float* __restrict__ kv,
@@ -81,26 +82,24 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_short_kernel(
     float v[8];
     if constexpr (kRatio == 1) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = x[0][e];
+        for (int e = 0; e < 8; ++e) v[e] = round_bf16(x[0][e]);
     } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float m = s[0][e];
 #pragma unroll
             for (int j = 1; j < kRatio; ++j) m = fmaxf(m, s[j][e]);
-            const float mb = m * kLog2e;
-            float den = 0.0f, num = 0.0f;
+            const double md = m;
+            double den = 0.0, num = 0.0;
 #pragma unroll
             for (int j = 0; j < kRatio; ++j) {
-                const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][e], kLog2e, -mb));
+                const double w = exp_f64(static_cast<double>(s[j][e]) - md);
                 den += w;
-                num = __builtin_fmaf(w, x[j][e], num);
+                num = __builtin_fma(w, static_cast<double>(x[j][e]), num);
             }
-            v[e] = num * __builtin_amdgcn_rcpf(den);
+            v[e] = pool_result(den, num);
         }
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = round_bf16(v[e]);
     rope_apply(v, cs, lane);
     if (!valid) return;
     quantize_store_row<L>(pool, static_cast<uint32_t>(slot), v, lane);
@@ -113,11 +112,11 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_short_kernel(
 // together -- measured on MI355X about 3 % faster than giving each wavefront a contiguous
 // slice.  Each wavefront double-buffers its chunks (the next chunk's loads are in flight
 // while the current one is folded in; a share of at most four chunks is loaded whole
-// before folding, which measured faster at ratio 64) and keeps a per-channel online softmax state --
-// running max m (log2 units), denominator l, numerator acc -- rescaling once per chunk
-// (the online form of the vLLM page's section 2).  The kWaves partial states are merged
-// through LDS by wavefront 0 -- the only LDS use in the library -- which then rounds,
-// rotates, quantises and stores the row.
+// before folding, which measured faster at ratio 64) and keeps a float64 online softmax
+// state per channel (the online form of the vLLM page's section 2; PoolF64).  Every
+// wavefront starts from the same reference, the window's first score row, so the partial
+// states normally merge by plain addition.  Wavefronts 1.. write their states to LDS and
+// wavefront 0 merges them, rounds, rotates, quantises and stores the row.
 template <int kChunk>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ kv, const float* __restrict__ score,
                                            int64_t base, int64_t ld, int lane, float (&x)[kChunk][8],
@@ -129,24 +128,21 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ kv, const f
     }
 }
 
-template <int kChunk>
-__device__ __forceinline__ void fold_chunk(const float (&x)[kChunk][8], const float (&s)[kChunk][8],
-                                           float (&m)[8], float (&l)[8], float (&acc)[8]) {
+// This lane's 8 channels (two-half mapping) of a channel-indexed row held in LDS.
+__device__ __forceinline__ void load_lds_f32x8(const float* row, int lane, float (&v)[8]) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float cm = s[0][e];
+    for (int h = 0; h < 2; ++h) {
+        const float4 a = *reinterpret_cast<const float4*>(row + h * kHalf + 4 * lane);
+        v[4 * h] = a.x; v[4 * h + 1] = a.y; v[4 * h + 2] = a.z; v[4 * h + 3] = a.w;
+    }
+}
+
+__device__ __forceinline__ void load_lds_f64x8(const double* row, int lane, double (&v)[8]) {
 #pragma unroll
-        for (int j = 1; j < kChunk; ++j) cm = fmaxf(cm, s[j][e]);
-        const float mn = fmaxf(m[e], cm * kLog2e);
-        const float alpha = __builtin_amdgcn_exp2f(m[e] - mn);
-        float le = l[e] * alpha, ae = acc[e] * alpha;
-#pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-            const float wt = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][e], kLog2e, -mn));
-            le += wt;
-            ae = __builtin_fmaf(wt, x[j][e], ae);
-        }
-        m[e] = mn; l[e] = le; acc[e] = ae;
+    for (int h = 0; h < 2; ++h) {
+        const double2 a = *reinterpret_cast<const double2*>(row + h * kHalf + 4 * lane);
+        const double2 b = *reinterpret_cast<const double2*>(row + h * kHalf + 4 * lane + 2);
+        v[4 * h] = a.x; v[4 * h + 1] = a.y; v[4 * h + 2] = b.x; v[4 * h + 3] = b.y;
     }
 }
 
@@ -158,7 +154,10 @@ __global__ __launch_bounds__(kWave * kWaves) void compress_long_kernel(
     int64_t R) {
     constexpr int kChunksPerWave = kRatio / (kWaves * kChunk);
     static_assert(kRatio % (kWaves * kChunk) == 0 && kChunksPerWave % 2 == 0, "window split");
-    __shared__ float4 part[kWaves - 1][3][kWave * 2];
+    // partial states of wavefronts 1..kWaves-1, channel-indexed
+    __shared__ __attribute__((aligned(16))) double part_l[kWaves - 1][kHeadDim];
+    __shared__ __attribute__((aligned(16))) double part_a[kWaves - 1][kHeadDim];
+    __shared__ __attribute__((aligned(16))) float part_r[kWaves - 1][kHeadDim];
 
     const int64_t i = blockIdx.x;
     const int32_t slot = slots[i];
@@ -167,12 +166,16 @@ __global__ __launch_bounds__(kWave * kWaves) void compress_long_kernel(
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = wave_id();
-    const int64_t base = (i * kRatio + static_cast<int64_t>(w) * kChunk) * ld;   // chunk w
-    const int64_t step = static_cast<int64_t>(kWaves) * kChunk * ld;            // to chunk w + kWaves
+    const int64_t row0 = i * kRatio * ld;
+    const int64_t base = row0 + static_cast<int64_t>(w) * kChunk * ld;   // chunk w
+    const int64_t step = static_cast<int64_t>(kWaves) * kChunk * ld;     // to chunk w + kWaves
 
-    float m[8], l[8], acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) { m[e] = -__builtin_inff(); l[e] = 0.0f; acc[e] = 0.0f; }
+    PoolF64 st;
+    {
+        float ref[8];
+        load_row_f32(score + row0, lane, ref);
+        pool_init(st, ref);
+    }
 
     if constexpr (kChunksPerWave <= 4) {
         // the wavefront's whole share fits in registers: issue every load, then fold
@@ -180,70 +183,109 @@ __global__ __launch_bounds__(kWave * kWaves) void compress_long_kernel(
 #pragma unroll
         for (int c = 0; c < kChunksPerWave; ++c) load_chunk<kChunk>(kv, score, base + c * step, ld, lane, x[c], sc[c]);
 #pragma unroll
-        for (int c = 0; c < kChunksPerWave; ++c) fold_chunk<kChunk>(x[c], sc[c], m, l, acc);
+        for (int c = 0; c < kChunksPerWave; ++c) pool_fold<kChunk>(st, x[c], sc[c]);
     } else {
         float xa[kChunk][8], sa[kChunk][8], xb[kChunk][8], sb[kChunk][8];
         load_chunk<kChunk>(kv, score, base, ld, lane, xa, sa);
 #pragma unroll 1
         for (int c = 0; c < kChunksPerWave; c += 2) {
             load_chunk<kChunk>(kv, score, base + (c + 1) * step, ld, lane, xb, sb);
-            fold_chunk<kChunk>(xa, sa, m, l, acc);
+            pool_fold<kChunk>(st, xa, sa);
             if (c + 2 < kChunksPerWave) load_chunk<kChunk>(kv, score, base + (c + 2) * step, ld, lane, xa, sa);
-            fold_chunk<kChunk>(xb, sb, m, l, acc);
+            pool_fold<kChunk>(st, xb, sb);
         }
     }
 
     RopeCS cs;
     if (w == 0) rope_load_cs(cos_sin + static_cast<int64_t>(p) * kRopeDim, lane, cs);
     if (w != 0) {
-        float4* dst = &part[w - 1][0][2 * lane];
-        dst[0] = make_float4(m[0], m[1], m[2], m[3]);
-        dst[1] = make_float4(m[4], m[5], m[6], m[7]);
-        dst = &part[w - 1][1][2 * lane];
-        dst[0] = make_float4(l[0], l[1], l[2], l[3]);
-        dst[1] = make_float4(l[4], l[5], l[6], l[7]);
-        dst = &part[w - 1][2][2 * lane];
-        dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int c0 = h * kHalf + 4 * lane;
+            double2* dl = reinterpret_cast<double2*>(&part_l[w - 1][c0]);
+            double2* da = reinterpret_cast<double2*>(&part_a[w - 1][c0]);
+            dl[0] = make_double2(st.l[4 * h], st.l[4 * h + 1]);
+            dl[1] = make_double2(st.l[4 * h + 2], st.l[4 * h + 3]);
+            da[0] = make_double2(st.acc[4 * h], st.acc[4 * h + 1]);
+            da[1] = make_double2(st.acc[4 * h + 2], st.acc[4 * h + 3]);
+            *reinterpret_cast<float4*>(&part_r[w - 1][c0]) =
+                make_float4(st.ref[4 * h], st.ref[4 * h + 1], st.ref[4 * h + 2], st.ref[4 * h + 3]);
+        }
     }
     __syncthreads();
     if (w != 0) return;
 
+    // merge: M = the largest reference per channel; a state on another reference is
+    // rescaled to it (rare: only after a score exceeded the first row's by kRefSlack).
+    // One partner at a time (no unrolling), so only its state is live in registers.
+    double M[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) M[e] = st.ref[e];
+#pragma unroll 1
+    for (int q = 0; q < kWaves - 1; ++q) {
+        float rq[8];
+        load_lds_f32x8(&part_r[q][0], lane, rq);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) M[e] = __builtin_fmax(M[e], static_cast<double>(rq[e]));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pool_rebase(st.ref[e], M[e], st.l[e], st.acc[e]);
+#pragma unroll 1
+    for (int q = 0; q < kWaves - 1; ++q) {
+        float rq[8];
+        double lq[8], aq[8];
+        load_lds_f32x8(&part_r[q][0], lane, rq);
+        load_lds_f64x8(&part_l[q][0], lane, lq);
+        load_lds_f64x8(&part_a[q][0], lane, aq);
+        bool moved = false;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) moved |= static_cast<double>(rq[e]) != M[e];
+        if (moved) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pool_rebase(rq[e], M[e], lq[e], aq[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            st.l[e] += lq[e];
+            st.acc[e] += aq[e];
+        }
+    }
     float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float pm[kWaves - 1], pl[kWaves - 1], pa[kWaves - 1];
-        float M = m[e];
-#pragma unroll
-        for (int q = 0; q < kWaves - 1; ++q) {
-            pm[q] = reinterpret_cast<const float*>(&part[q][0][2 * lane])[e];
-            pl[q] = reinterpret_cast<const float*>(&part[q][1][2 * lane])[e];
-            pa[q] = reinterpret_cast<const float*>(&part[q][2][2 * lane])[e];
-            M = fmaxf(M, pm[q]);
-        }
-        const float a0 = __builtin_amdgcn_exp2f(m[e] - M);
-        float den = l[e] * a0, num = acc[e] * a0;
-#pragma unroll
-        for (int q = 0; q < kWaves - 1; ++q) {
-            const float a = __builtin_amdgcn_exp2f(pm[q] - M);
-            den = __builtin_fmaf(pl[q], a, den);
-            num = __builtin_fmaf(pa[q], a, num);
-        }
-        v[e] = round_bf16(num * __builtin_amdgcn_rcpf(den));
-    }
+    for (int e = 0; e < 8; ++e) v[e] = pool_result(st.l[e], st.acc[e]);
     rope_apply(v, cs, lane);
     quantize_store_row<L>(pool, static_cast<uint32_t>(slot), v, lane);
 }
 
 // ------------------------------------------------------------------ decode-step compressor state
-// One row per state (sequence) per call: fold the row into the state's online softmax
-// (m in log2 units, l, acc per channel; 3 x 512 fp32 in channel order), count it, and
-// when the window is complete, finalise like the window kernels (acc / l rounded to bf16,
-// RoPE at the completing row's position, quantise, store at its slot) and reset the
-// count.  count == 0 means an empty state, so a zeroed buffer is a valid start.
+// One row per state (sequence) per call: fold the row into the state's float64 online
+// softmax (reference score, l and acc per channel, as PoolF64), count it, and when the
+// window is complete, finalise like the window kernels (acc / l rounded once to bf16, RoPE
+// at the completing row's position, quantise, store at its slot) and reset the count.
+// State layout, kStateBytes per sequence: ref fp32 [512], l fp64 [512], acc fp64 [512].
+// count == 0 means an empty state, so a zeroed buffer is a valid start.
+constexpr int64_t kStateBytes = kHeadDim * (4 + 8 + 8);
+
+__device__ __forceinline__ void load_f64x8(const double* __restrict__ row, int lane, double (&v)[8]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const double2 a = *reinterpret_cast<const double2*>(row + h * kHalf + 4 * lane);
+        const double2 b = *reinterpret_cast<const double2*>(row + h * kHalf + 4 * lane + 2);
+        v[4 * h] = a.x; v[4 * h + 1] = a.y; v[4 * h + 2] = b.x; v[4 * h + 3] = b.y;
+    }
+}
+
+__device__ __forceinline__ void store_f64x8(double* __restrict__ row, int lane, const double (&v)[8]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        *reinterpret_cast<double2*>(row + h * kHalf + 4 * lane) = make_double2(v[4 * h], v[4 * h + 1]);
+        *reinterpret_cast<double2*>(row + h * kHalf + 4 * lane + 2) = make_double2(v[4 * h + 2], v[4 * h + 3]);
+    }
+}
+
 template <Layout L>
 __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_state_kernel(
-    uint8_t* __restrict__ pool, int64_t nslots, float* __restrict__ state, int32_t* __restrict__ count,
+    uint8_t* __restrict__ pool, int64_t nslots, uint8_t* __restrict__ state, int32_t* __restrict__ count,
     int64_t num_states, int32_t ratio, const int32_t* __restrict__ state_ids, const float* __restrict__ kv,
     const float* __restrict__ score, int64_t ld, const int32_t* __restrict__ pos,
     const float* __restrict__ cos_sin, int64_t max_pos, const int32_t* __restrict__ slots, int64_t n) {
@@ -255,35 +297,41 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_state_kernel(
     float x[8], s[8];
     load_row_f32(kv + j * ld, lane, x);
     load_row_f32(score + j * ld, lane, s);
-    float* st = state + static_cast<int64_t>(sid) * 3 * kHeadDim;
+    uint8_t* st = state + static_cast<int64_t>(sid) * kStateBytes;
+    float* st_ref = reinterpret_cast<float*>(st);
+    double* st_l = reinterpret_cast<double*>(st + kHeadDim * 4);
+    double* st_a = reinterpret_cast<double*>(st + kHeadDim * 12);
     const int32_t c = count[sid];
-    float m[8], l[8], acc[8];
+    float ref[8];
+    double l[8], acc[8];
     if (c == 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { m[e] = s[e] * kLog2e; l[e] = 1.0f; acc[e] = x[e]; }
+        for (int e = 0; e < 8; ++e) { ref[e] = s[e]; l[e] = 1.0; acc[e] = x[e]; }
     } else {
-        float pm[8], pl[8], pa[8];
-        load_row_f32(st, lane, pm);
-        load_row_f32(st + kHeadDim, lane, pl);
-        load_row_f32(st + 2 * kHeadDim, lane, pa);
+        float r0[8];
+        *reinterpret_cast<float4*>(&r0[0]) = *reinterpret_cast<const float4*>(st_ref + 4 * lane);
+        *reinterpret_cast<float4*>(&r0[4]) = *reinterpret_cast<const float4*>(st_ref + kHalf + 4 * lane);
+        load_f64x8(st_l, lane, l);
+        load_f64x8(st_a, lane, acc);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float mn = fmaxf(pm[e], s[e] * kLog2e);
-            const float alpha = __builtin_amdgcn_exp2f(pm[e] - mn);
-            const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], kLog2e, -mn));
-            m[e] = mn;
-            l[e] = __builtin_fmaf(pl[e], alpha, w);
-            acc[e] = __builtin_fmaf(pa[e], alpha, w * x[e]);
+            ref[e] = r0[e];
+            if (s[e] > ref[e] + kRefSlack) {
+                const double a = exp_f64(static_cast<double>(ref[e]) - static_cast<double>(s[e]));
+                l[e] *= a;
+                acc[e] *= a;
+                ref[e] = s[e];
+            }
+            const double w = exp_f64(static_cast<double>(s[e]) - static_cast<double>(ref[e]));
+            l[e] += w;
+            acc[e] = __builtin_fma(w, static_cast<double>(x[e]), acc[e]);
         }
     }
     if (c + 1 < ratio) {
-        float* dst[3] = {st, st + kHeadDim, st + 2 * kHeadDim};
-        const float* src[3] = {m, l, acc};
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            *reinterpret_cast<float4*>(dst[q] + 4 * lane) = make_float4(src[q][0], src[q][1], src[q][2], src[q][3]);
-            *reinterpret_cast<float4*>(dst[q] + kHalf + 4 * lane) = make_float4(src[q][4], src[q][5], src[q][6], src[q][7]);
-        }
+        *reinterpret_cast<float4*>(st_ref + 4 * lane) = make_float4(ref[0], ref[1], ref[2], ref[3]);
+        *reinterpret_cast<float4*>(st_ref + kHalf + 4 * lane) = make_float4(ref[4], ref[5], ref[6], ref[7]);
+        store_f64x8(st_l, lane, l);
+        store_f64x8(st_a, lane, acc);
         if (lane == 0) count[sid] = c + 1;
         return;
     }
@@ -295,7 +343,7 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_state_kernel(
     rope_load_cs(cos_sin + static_cast<int64_t>(valid ? p : 0) * kRopeDim, lane, cs);
     float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = round_bf16(acc[e] * __builtin_amdgcn_rcpf(l[e]));
+    for (int e = 0; e < 8; ++e) v[e] = pool_result(l[e], acc[e]);
     rope_apply(v, cs, lane);
     if (!valid) return;
     quantize_store_row<L>(pool, static_cast<uint32_t>(slot), v, lane);

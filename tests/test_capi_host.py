@@ -232,3 +232,51 @@ def test_oversized_page_count_is_rejected(kvq):
                                       None) == kvq.KVQ_EINVAL
     assert L.kv_dequant(V41, A, big, B, 1, C, None) == kvq.KVQ_EINVAL
     assert L.kv_dequant_slots(V41, A, big, B, 1, C, None) == kvq.KVQ_EINVAL
+
+
+def test_build_id_matches_the_sources(kvq):
+    """The loaded library was built from the sources next to it."""
+    from quantized_paged_kv_compress_amd import _build
+    lib = ctypes.CDLL(kvq.LIB_PATH)
+    lib.kvq_build_id.restype = ctypes.c_char_p
+    assert lib.kvq_build_id().decode() == _build.source_hash()
+    assert len(_build.source_hash()) == 64
+
+
+def test_stale_library_is_refused(kvq, monkeypatch):
+    """A library whose build id differs from the current sources' hash is not loaded."""
+    import quantized_paged_kv_compress_amd as m
+    from quantized_paged_kv_compress_amd import _build
+    monkeypatch.setattr(m, "_lib", None)
+    monkeypatch.setattr(_build, "source_hash", lambda: "0" * 64)
+    with pytest.raises(ImportError, match="stale"):
+        m.load_library()
+
+
+def test_compress_state_bytes(kvq):
+    assert kvq.compress_state_bytes() == 512 * (4 + 8 + 8)
+
+
+def test_sizes_beyond_one_launch_are_rejected(kvq):
+    """Each entry point refuses, on the host and before anything is enqueued, a request
+    larger than its grid can cover (2^32 work-items in x); the limits are the header's."""
+    L = kvq.load_library()
+    max_rows, max_long, max_pages = 1 << 25, 1 << 22, 1 << 19
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    assert f"#define KVQ_MAX_ROWS {max_rows}" in src
+    assert f"#define KVQ_MAX_LONG_ROWS {max_long}" in src
+    assert f"#define KVQ_MAX_PAGES {max_pages}" in src
+    big = max_rows + 1
+    assert L.kv_store(V41, A, 4, B, 512, C, big, None) == kvq.KVQ_EINVAL
+    assert L.kv_store_rope(V41, A, 4, B, 512, C, A, 10, C, big, None) == kvq.KVQ_EINVAL
+    assert L.kv_store_norm_rope(V41, A, 4, B, 512, C, 1e-6, A, B, 10, C, big, None) == kvq.KVQ_EINVAL
+    assert L.kv_dequant_slots(V41, A, 4, B, big, C, None) == kvq.KVQ_EINVAL
+    assert L.kv_compress_state_update(V41, A, 4, B, C, 8, 4, A, B, C, 512, A, B, 10, C, big,
+                                      None) == kvq.KVQ_EINVAL
+    for ratio in (1, 2, 4):
+        assert L.kv_compress_store(V41, A, 4, B, C, 512, ratio, A, B, 10, C, big, None) == kvq.KVQ_EINVAL
+    for ratio in (8, 16, 32, 64, 128):
+        assert L.kv_compress_store(V41, A, 4, B, C, 512, ratio, A, B, 10, C, max_long + 1,
+                                   None) == kvq.KVQ_EINVAL
+    assert L.kv_dequant(V41, A, 4, B, max_pages + 1, C, None) == kvq.KVQ_EINVAL
+    assert L.kv_translate_slots(A, 100, B, 5, C, 1 << 31, None) == kvq.KVQ_EINVAL

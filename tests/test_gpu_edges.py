@@ -53,7 +53,7 @@ def test_boundary_slots_and_positions_store_paths(kvq, orc, cs_small, layout):
         got = to_host(pool)
         if name == "norm":
             valid = (EDGE_SLOTS >= 0) & (EDGE_SLOTS < NUM_PAGES * 64) & (pos >= 0) & (pos < 100)
-            compare_compressed(got, ref, layout, EDGE_SLOTS[valid], None, label=f"edge norm L{layout}")
+            compare_compressed(got, ref, layout, EDGE_SLOTS[valid], label=f"edge norm L{layout}")
             assert untouched_equal(got, ref, layout, EDGE_SLOTS[valid])
         else:
             assert np.array_equal(got, ref), name
@@ -73,9 +73,7 @@ def test_boundary_slots_compress(kvq, orc, cs_small, layout, ratio):
     orc.kv_compress_store(layout, ref, kv, sc, ratio, pos, cs_small, EDGE_SLOTS)
     got = to_host(pool)
     valid = (EDGE_SLOTS >= 0) & (EDGE_SLOTS < NUM_PAGES * 64) & (pos >= 0) & (pos < 100)
-    f64, _ = orc.pool_rows(kv, sc, ratio)
-    compare_compressed(got, ref, layout, EDGE_SLOTS[valid], f64[valid], label=f"edge slots r{ratio}",
-                       rope=(pos[valid], cs_small))
+    compare_compressed(got, ref, layout, EDGE_SLOTS[valid], label=f"edge slots r{ratio}")
     assert untouched_equal(got, ref, layout, EDGE_SLOTS[valid])
 
 
@@ -114,8 +112,7 @@ def test_compress_extreme_values(kvq, orc, layout, ratio):
     kvq.kv_compress_store(pool, layout, to_dev(kv), to_dev(sc), ratio, to_dev(pos), to_dev(cs), to_dev(slots))
     ref = orc.new_pool(layout, NUM_PAGES)
     orc.kv_compress_store(layout, ref, kv, sc, ratio, pos, cs, slots)
-    f64, _ = orc.pool_rows(kv, sc, ratio)
-    compare_compressed(to_host(pool), ref, layout, slots, f64, label=f"extreme r{ratio} L{layout}", rope=(pos, cs))
+    compare_compressed(to_host(pool), ref, layout, slots, label=f"extreme r{ratio} L{layout}")
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
@@ -145,10 +142,8 @@ def test_compress_state_edges(kvq, orc, layout):
     ref = orc.new_pool(layout, NUM_PAGES)
     orc.kv_compress_store(layout, ref, kv, sc, ratio, pos, cs, slots)
     valid = slots < NUM_PAGES * 64
-    f64, _ = orc.pool_rows(kv, sc, ratio)
     got = to_host(pool)
-    compare_compressed(got, ref, layout, slots[valid], f64[valid], label=f"state edges L{layout}",
-                       rope=(pos[valid], cs))
+    compare_compressed(got, ref, layout, slots[valid], label=f"state edges L{layout}")
     assert untouched_equal(got, ref, layout, slots[valid])
 
 
@@ -206,9 +201,8 @@ def test_pool_larger_than_4gib(kvq, orc, cs_small):
     kvq.kv_compress_store(pool, V41, to_dev(kv), to_dev(sc), 4, to_dev(pos), to_dev(cs_small), to_dev(slots))
     ref2 = orc.new_pool(V41, pages.size)
     orc.kv_compress_store(V41, ref2, kv, sc, 4, pos, cs_small, small_slots)
-    f64, _ = orc.pool_rows(kv, sc, 4)
     got2 = to_host(pool[torch.from_numpy(pages).to("cuda")])
-    compare_compressed(got2, ref2, V41, small_slots, f64, label="pool > 4 GiB", rope=(pos, cs_small))
+    compare_compressed(got2, ref2, V41, small_slots, label="pool > 4 GiB")
     del pool
     torch.cuda.empty_cache()
 
@@ -319,5 +313,4 @@ def test_compress_score_spread(kvq, orc, ratio, sigma):
     kvq.kv_compress_store(pool, V41, to_dev(kv), to_dev(sc), ratio, to_dev(pos), to_dev(cs), to_dev(slots))
     ref = orc.new_pool(V41, NUM_PAGES)
     orc.kv_compress_store(V41, ref, kv, sc, ratio, pos, cs, slots)
-    f64, _ = orc.pool_rows(kv, sc, ratio)
-    compare_compressed(to_host(pool), ref, V41, slots, f64, label=f"spread {sigma} r{ratio}", rope=(pos, cs))
+    compare_compressed(to_host(pool), ref, V41, slots, label=f"spread {sigma} r{ratio}")

@@ -191,10 +191,7 @@ def test_store_norm_rope_within_tolerance(kvq, orc, cos_sin, cos_sin_dev, layout
     kvq.kv_store_norm_rope(pool, layout, to_dev(k), to_dev(w), eps, to_dev(pos), cos_sin_dev, to_dev(slots))
     orc.kv_store_norm_rope(layout, ref, k, w, eps, pos, cos_sin, slots)
     got = to_host(pool)
-    xv = (k.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    wv = (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    exact = xv * wv / np.sqrt((xv * xv).mean(axis=1, keepdims=True) + eps)
-    compare_compressed(got, ref, layout, slots, exact, label=f"norm n{n} L{layout}", rope=(pos, cos_sin))
+    compare_compressed(got, ref, layout, slots, label=f"norm n{n} L{layout}")
     assert untouched_equal(got, ref, layout, slots)
 
 
@@ -238,8 +235,7 @@ def test_compress_small_within_tolerance(kvq, orc, cos_sin, cos_sin_dev, layout,
     slots = wl.distinct_slots(rng, R, 64, num_pages * 64)
     log(f"[compress] ratio {ratio}, R {R}, layout {layout}")
     got, ref = run_compress(kvq, orc, layout, ratio, kv, sc, pos, slots, num_pages, cos_sin, cos_sin_dev)
-    f64, _ = orc.pool_rows(kv, sc, ratio)
-    compare_compressed(got, ref, layout, slots, f64, label=f"r{ratio} R{R} L{layout}", rope=(pos, cos_sin))
+    compare_compressed(got, ref, layout, slots, label=f"r{ratio} R{R} L{layout}")
     assert untouched_equal(got, ref, layout, slots)
 
 
@@ -265,17 +261,15 @@ def test_compress_skips_invalid_rows_and_honours_stride(kvq, orc, cos_sin, cos_s
     kv, sc = np.ascontiguousarray(kvw[:, :512]), np.ascontiguousarray(scw[:, :512])
     orc.kv_compress_store(layout, ref, kv, sc, ratio, pos, short, slots)
     valid = (slots >= 0) & (slots < num_pages * 64) & (pos >= 0) & (pos < 4000)
-    f64, _ = orc.pool_rows(kv, sc, ratio)
-    compare_compressed(got, ref, layout, slots[valid], f64[valid], label="stride/skip", rope=(pos[valid], short))
+    compare_compressed(got, ref, layout, slots[valid], label="stride/skip")
     assert untouched_equal(got, ref, layout, slots[valid])
     torch.cuda.synchronize()
 
 
 def full_compressor_check(kvq, orc, layout, ratio, R, seed, cos_sin, cos_sin_dev, num_pages=4096):
     """Full-size workload, launched as the benchmark launches it, compared on every output
-    row.  Pass 1 generates the inputs chunk by chunk, uploads them and lets the oracle
-    write its pool; after the launch, pass 2 regenerates each chunk for the exact pooled
-    values and compares that chunk's rows, so no full-size host copy is ever held."""
+    row.  The inputs are generated chunk by chunk, uploaded, and the oracle writes its pool
+    from each chunk, so no full-size host copy of the inputs is ever held."""
     import torch
     meta = wl.compressor_meta(seed, R, num_pages)
     log(f"[full] ratio {ratio} R {R}: generating inputs, oracle on every row")
@@ -297,12 +291,7 @@ def full_compressor_check(kvq, orc, layout, ratio, R, seed, cos_sin, cos_sin_dev
     torch.cuda.synchronize()
     got = to_host(pool)
     del kv, sc, pool
-    for i0, n in chunks:
-        a, b = wl.compressor_window(seed, ratio, i0, n)
-        f64 = orc.pool_rows(a, b, ratio)[0]
-        compare_compressed(got, ref, layout, meta["slots"][i0:i0 + n], f64,
-                           label=f"full r{ratio} L{layout} rows {i0}+{n}",
-                           rope=(meta["pos"][i0:i0 + n], cos_sin))
+    compare_compressed(got, ref, layout, meta["slots"], label=f"full r{ratio} L{layout} R {R}")
     assert untouched_equal(got, ref, layout, meta["slots"])   # nothing outside the slots
 
 
@@ -368,7 +357,7 @@ def test_compress_state_decode_steps(kvq, orc, cos_sin, cos_sin_dev, layout, rat
     got = to_host(pool)
     assert np.array_equal(to_host(count)[sid_of], (nrows % ratio).astype(np.int32))
     ref = orc.new_pool(layout, num_pages)
-    done_slots, done_pos, f64s = [], [], []
+    done_slots = []
     for s_ in range(S):
         if nwin[s_] == 0:
             continue
@@ -378,12 +367,9 @@ def test_compress_state_decode_steps(kvq, orc, cos_sin, cos_sin_dev, layout, rat
         orc.kv_compress_store(layout, ref, kvw, scw, ratio, np.ascontiguousarray(win_pos[s_][:nwin[s_]]),
                               cos_sin, sl)
         done_slots.append(sl)
-        done_pos.append(win_pos[s_][:nwin[s_]])
-        f64s.append(orc.pool_rows(kvw, scw, ratio)[0])
     done = np.concatenate(done_slots)
     log(f"[state] ratio {ratio}: {done.size} windows completed over {T} steps")
-    compare_compressed(got, ref, layout, done, np.concatenate(f64s), label=f"state r{ratio} L{layout}",
-                       rope=(np.concatenate(done_pos), cos_sin))
+    compare_compressed(got, ref, layout, done, label=f"state r{ratio} L{layout}")
     assert untouched_equal(got, ref, layout, done)   # incomplete windows wrote nothing
 
 
@@ -502,8 +488,7 @@ def test_mixed_fp4_step(kvq, orc, cos_sin, cos_sin_dev):
     slots = ref_loc[:R].copy()
     ref_pool = orc.new_pool(FP4, d["num_pages"])
     orc.kv_compress_store(FP4, ref_pool, d["kv"], d["score"], 4, d["pos"], cos_sin, slots)
-    f64, _ = orc.pool_rows(d["kv"], d["score"], 4)
-    compare_compressed(got_pool, ref_pool, FP4, slots, f64, label="mixed fp4", rope=(d["pos"], cos_sin))
+    compare_compressed(got_pool, ref_pool, FP4, slots, label="mixed fp4")
     assert untouched_equal(got_pool, ref_pool, FP4, slots)
     assert np.array_equal(to_host(ws), orc.kv_dequant(FP4, got_pool, d["page_ids"]))
 
@@ -532,6 +517,5 @@ def test_compress_state_bench_shape(kvq, orc, cos_sin, cos_sin_dev, layout):
     ref = orc.new_pool(layout, num_pages)
     orc.kv_compress_store(layout, ref, kv, sc, ratio, pos, cos_sin, slots)
     got = to_host(pool)
-    compare_compressed(got, ref, layout, slots, orc.pool_rows(kv, sc, ratio)[0],
-                       label=f"state bench shape L{layout}", rope=(pos, cos_sin))
+    compare_compressed(got, ref, layout, slots, label=f"state bench shape L{layout}")
     assert untouched_equal(got, ref, layout, slots)

@@ -1,58 +1,90 @@
-"""The parity rules themselves, pinned on the CPU with constructed cases: the RoPE-channel
-rule must admit exactly the codes that the other admissible bf16 rounding of a rotation
-input produces, and nothing else."""
-import math
-
+"""The compressor comparison rule itself, pinned on the CPU with constructed pools: it
+passes identical pools and one-step code differences under 0.1 %, and rejects any scale
+byte difference, any code two or more steps away, and one-step differences above 0.1 %."""
 import numpy as np
+import pytest
 
-import oracle
-from helpers import V41, _bf16_neighbours, _ord, near_bf16_midpoint, rope_alternative_ok
-from quantized_paged_kv_compress_amd import workloads as wl
-
-SCALE_BYTE = 119          # ue8m0 k = -8: blocks whose largest value is near 1
+from helpers import CR, FP4, SR, V41, compare_compressed
 
 
-def _setup():
-    """Rotation pair 0 at position 1 (angle 1 rad): x1 (channel 448) just above the
-    midpoint of two bf16 neighbours, x2 (channel 480) the bf16 value that nearly cancels
-    x1 in o2 = x2*c + x1*s."""
-    cs = wl.rope_cos_sin(max_pos=4)
-    pos = 1
-    c, s = float(cs[pos, 0]), float(cs[pos, 32])
-    lo, q = 103 / 256, 2.0 ** -9                     # a bf16 value in [0.25, 0.5) and its spacing
-    x1 = lo + 0.5 * q * (1 + 2.0 ** -30)
-    x2 = oracle.bf16_to_f32(oracle.bf16_from_double(-x1 * s / c))
-    row = np.zeros(512)
-    row[448], row[480] = x1, x2
-    return cs, pos, row
+def _pools(layout, n=64, seed=0):
+    rng = np.random.default_rng(seed)
+    pb = 64 * (CR[layout] + SR[layout])
+    pool = np.zeros((2, pb), np.uint8)
+    slots = np.arange(64, 64 + n, dtype=np.int32)
+    for s in slots:
+        page, row = divmod(int(s), 64)
+        codes = rng.integers(0, 256, CR[layout]).astype(np.uint8)
+        if layout == V41:
+            codes[(codes & 0x7F) == 0x7F] = 0x10          # no NaN codes
+        pool[page, row * CR[layout]:(row + 1) * CR[layout]] = codes
+        pool[page, 64 * CR[layout] + row * SR[layout]:64 * CR[layout] + row * SR[layout] + 16] = \
+            rng.integers(100, 140, 16)
+    return pool, slots
 
 
-def _code(b1, b2, cs, pos, ch):
-    v = np.zeros(512, np.uint16)
-    v[448], v[480] = b1, b2
-    val = oracle.bf16_to_f32(int(oracle.rope_row(v, cs[pos])[ch]))
-    return _ord(oracle.e4m3_encode(math.ldexp(val, -(SCALE_BYTE - 127))), V41)
+def _code_offset(layout, row, byte):
+    return row * CR[layout] + byte
 
 
-def test_bf16_neighbours_bracket_the_value():
-    for x in (0.3, -0.3, 1e-3, 123.456, 2.0 ** -130):
-        a, b = (oracle.bf16_to_f32(n) for n in _bf16_neighbours(x))
-        assert min(a, b) <= x <= max(a, b) and a != b
+@pytest.mark.parametrize("layout", [V41, FP4])
+def test_identical_pools_pass(layout):
+    pool, slots = _pools(layout)
+    assert compare_compressed(pool, pool.copy(), layout, slots) == 1.0
 
 
-def test_rope_rule_admits_the_other_rounding_and_nothing_else():
-    cs, pos, row = _setup()
-    assert near_bf16_midpoint(row[448]) and not near_bf16_midpoint(row[480])
-    b2 = oracle.bf16_from_double(row[480])
-    b_rne = oracle.bf16_from_double(row[448])
-    b_alt = [b for b in _bf16_neighbours(row[448]) if b != b_rne][0]
-    o_rne, o_alt = _code(b_rne, b2, cs, pos, 480), _code(b_alt, b2, cs, pos, 480)
-    assert abs(o_rne - o_alt) > 1          # the rotation amplifies one bf16 ulp (precondition)
-    for got in (o_rne, o_alt, o_alt + 1 if o_alt > o_rne else o_alt - 1):
-        assert rope_alternative_ok(V41, got, SCALE_BYTE, row, 480, pos, cs)
-    far = max(o_rne, o_alt) + 3
-    assert not rope_alternative_ok(V41, far, SCALE_BYTE, row, 480, pos, cs)
-    # the same code with no input at a near-tie is not excused
-    row2 = row.copy()
-    row2[448] = 103 / 256 + 0.25 * 2.0 ** -9
-    assert not rope_alternative_ok(V41, o_alt, SCALE_BYTE, row2, 480, pos, cs)
+def test_signed_zero_codes_are_equal():
+    pool, slots = _pools(V41)
+    a, b = pool.copy(), pool.copy()
+    a[1, _code_offset(V41, 0, 5)] = 0x00
+    b[1, _code_offset(V41, 0, 5)] = 0x80
+    assert compare_compressed(a, b, V41, slots) == 1.0
+
+
+@pytest.mark.parametrize("layout", [V41, FP4])
+def test_a_scale_byte_difference_fails(layout):
+    pool, slots = _pools(layout)
+    b = pool.copy()
+    b[1, 64 * CR[layout] + 3 * SR[layout] + 7] ^= 1
+    with pytest.raises(AssertionError, match="scale bytes differ"):
+        compare_compressed(pool, b, layout, slots)
+
+
+def test_two_code_steps_fail_and_one_passes():
+    pool, slots = _pools(V41)
+    a, b = pool.copy(), pool.copy()
+    a[1, _code_offset(V41, 2, 9)] = 0x20
+    b[1, _code_offset(V41, 2, 9)] = 0x21
+    assert compare_compressed(a, b, V41, slots) < 1.0          # one step: admitted
+    b[1, _code_offset(V41, 2, 9)] = 0x22
+    with pytest.raises(AssertionError, match="more than one step"):
+        compare_compressed(a, b, V41, slots)
+    b[1, _code_offset(V41, 2, 9)] = 0xA1                      # -1 vs +0x20: far apart
+    with pytest.raises(AssertionError, match="more than one step"):
+        compare_compressed(a, b, V41, slots)
+
+
+def test_fp4_nibbles_are_compared_one_by_one():
+    pool, slots = _pools(FP4)
+    a, b = pool.copy(), pool.copy()
+    a[1, _code_offset(FP4, 4, 0)] = 0x32        # low nibble 2, high nibble 3
+    b[1, _code_offset(FP4, 4, 0)] = 0x23        # low 3 (one step), high 2 (one step)
+    assert compare_compressed(a, b, FP4, slots) < 1.0
+    b[1, _code_offset(FP4, 4, 0)] = 0x34        # low nibble 4: two steps
+    with pytest.raises(AssertionError, match="more than one step"):
+        compare_compressed(a, b, FP4, slots)
+    b[1, _code_offset(FP4, 4, 0)] = 0xB2        # high nibble -3 vs 3
+    with pytest.raises(AssertionError, match="more than one step"):
+        compare_compressed(a, b, FP4, slots)
+
+
+def test_too_many_one_step_differences_fail():
+    pool, slots = _pools(V41, n=4)               # 2048 codes: 0.1 % is 2 codes
+    a, b = pool.copy(), pool.copy()
+    for j in range(3):
+        a[1, _code_offset(V41, 1, j)] = 0x30
+        b[1, _code_offset(V41, 1, j)] = 0x31
+    with pytest.raises(AssertionError, match="identical"):
+        compare_compressed(a, b, V41, slots)
+    b[1, _code_offset(V41, 1, 2)] = 0x30
+    compare_compressed(a, b, V41, slots)
