@@ -35,7 +35,7 @@
  *    kv_translate_slots, which still zeroes out[0:cap].
  *  - Sizes above what one launch covers are refused with KVQ_EINVAL before anything is
  *    enqueued: rows n (or R) <= KVQ_MAX_ROWS, except R <= KVQ_MAX_LONG_ROWS for
- *    compressor ratios of 8 and more; pages P <= KVQ_MAX_PAGES; cap <= 2^31 - 1.
+ *    compressor ratios of 64 and more; pages P <= KVQ_MAX_PAGES; cap <= 2^31 - 1.
  *  - Inputs must be finite, with |kv| no larger than the largest finite bf16
  *    (about 3.39e38) so that no pooled value rounds to infinity; values outside that
  *    domain give unspecified codes.  fp32 denormals are handled.
@@ -79,7 +79,7 @@ extern "C" {
 
 /* ---- size limits of one call (larger requests return KVQ_EINVAL) --------------- */
 #define KVQ_MAX_ROWS 33554432      /* 2^25 rows of a store / gather / short-window call */
-#define KVQ_MAX_LONG_ROWS 4194304  /* 2^22 output rows of a compressor call, ratio >= 8 */
+#define KVQ_MAX_LONG_ROWS 4194304  /* 2^22 output rows of a compressor call, ratio >= 64 */
 #define KVQ_MAX_PAGES 524288       /* 2^19 page ids of one kv_dequant call              */
 
 /* ---- layout ids ---------------------------------------------------------------- */

@@ -19,8 +19,8 @@ namespace {
 using kvq::Layout;
 
 // Largest request of one call: each kernel's grid must stay below 2^32 work-items in x
-// (64 per row for the row kernels, 512 per output row for the long-window compressor,
-// 64 per row of each listed page for the page dequant).
+// (64 per row for the row kernels, up to 512 per output row for the workgroup-per-row
+// compressor of ratios 64 and 128, 64 per row of each listed page for the page dequant).
 constexpr int64_t kMaxRows = KVQ_MAX_ROWS;
 constexpr int64_t kMaxLongRows = KVQ_MAX_LONG_ROWS;
 constexpr int64_t kMaxDequantPages = KVQ_MAX_PAGES;
@@ -82,20 +82,28 @@ int store_impl(int mode, void* pool, int64_t num_pages, const uint16_t* k, int64
                   eps, pos, cos_sin, max_pos, slots, n);
 }
 
-template <Layout L, int kRatio>
-int compress_short(void* pool, int64_t num_pages, const float* kv, const float* score, int64_t ld,
-                   const int32_t* pos, const float* cos_sin, int64_t max_pos,
-                   const int32_t* slots, int64_t R, void* stream) {
-    return launch(kvq::compress_short_kernel<L, kRatio>, dim3(blocks_for(R, kvq::kRowsPerBlock)),
+template <Layout L>
+int compress_c1(void* pool, int64_t num_pages, const float* kv, int64_t ld, const int32_t* pos,
+                const float* cos_sin, int64_t max_pos, const int32_t* slots, int64_t R, void* stream) {
+    return launch(kvq::compress_c1_kernel<L>, dim3(blocks_for(R, kvq::kRowsPerBlock)),
+                  dim3(kvq::kWave * kvq::kRowsPerBlock), stream, static_cast<uint8_t*>(pool),
+                  num_pages << kvq::kPageBits, kv, ld, pos, cos_sin, max_pos, slots, R);
+}
+
+template <Layout L, int kRatio, int kChunk, int kDepth>
+int compress_wave(void* pool, int64_t num_pages, const float* kv, const float* score, int64_t ld,
+                  const int32_t* pos, const float* cos_sin, int64_t max_pos,
+                  const int32_t* slots, int64_t R, void* stream) {
+    return launch(kvq::compress_wave_kernel<L, kRatio, kChunk, kDepth>, dim3(blocks_for(R, kvq::kRowsPerBlock)),
                   dim3(kvq::kWave * kvq::kRowsPerBlock), stream, static_cast<uint8_t*>(pool),
                   num_pages << kvq::kPageBits, kv, score, ld, pos, cos_sin, max_pos, slots, R);
 }
 
-template <Layout L, int kRatio, int kWaves, int kChunk>
+template <Layout L, int kRatio, int kWaves, int kChunk, int kDepth>
 int compress_long(void* pool, int64_t num_pages, const float* kv, const float* score, int64_t ld,
                   const int32_t* pos, const float* cos_sin, int64_t max_pos,
                   const int32_t* slots, int64_t R, void* stream) {
-    return launch(kvq::compress_long_kernel<L, kRatio, kWaves, kChunk>, dim3(static_cast<unsigned>(R)),
+    return launch(kvq::compress_long_kernel<L, kRatio, kWaves, kChunk, kDepth>, dim3(static_cast<unsigned>(R)),
                   dim3(kvq::kWave * kWaves), stream, static_cast<uint8_t*>(pool),
                   num_pages << kvq::kPageBits, kv, score, ld, pos, cos_sin, max_pos, slots, R);
 }
@@ -104,15 +112,18 @@ template <Layout L>
 int compress_dispatch(int32_t ratio, void* pool, int64_t num_pages, const float* kv,
                       const float* score, int64_t ld, const int32_t* pos, const float* cos_sin,
                       int64_t max_pos, const int32_t* slots, int64_t R, void* stream) {
+    // per ratio: wave <rows per chunk, chunks in flight + 1>, long <wavefronts, rows per
+    // chunk, chunks in flight + 1>; measured fastest on MI355X
+    const auto* sc = score;
     switch (ratio) {
-        case 1: return compress_short<L, 1>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
-        case 2: return compress_short<L, 2>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
-        case 4: return compress_short<L, 4>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
-        case 8: return compress_long<L, 8, 4, 1>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
-        case 16: return compress_long<L, 16, 4, 2>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
-        case 32: return compress_long<L, 32, 8, 2>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
-        case 64: return compress_long<L, 64, 8, 2>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
-        case 128: return compress_long<L, 128, 8, 2>(pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 1: return compress_c1<L>(pool, num_pages, kv, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 2: return compress_wave<L, 2, 1, 2>(pool, num_pages, kv, sc, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 4: return compress_wave<L, 4, 2, 2>(pool, num_pages, kv, sc, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 8: return compress_wave<L, 8, 2, 4>(pool, num_pages, kv, sc, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 16: return compress_wave<L, 16, 2, 4>(pool, num_pages, kv, sc, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 32: return compress_wave<L, 32, 1, 4>(pool, num_pages, kv, sc, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 64: return compress_long<L, 64, 2, 2, 3>(pool, num_pages, kv, sc, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 128: return compress_long<L, 128, 4, 1, 3>(pool, num_pages, kv, sc, ld, pos, cos_sin, max_pos, slots, R, stream);
         default: return KVQ_ERATIO;
     }
 }
@@ -217,7 +228,7 @@ int kv_compress_store(int32_t layout, void* pool, int64_t num_pages, const float
     if (ratio != 1 && ratio != 2 && ratio != 4 && ratio != 8 && ratio != 16 && ratio != 32 &&
         ratio != 64 && ratio != 128)
         return KVQ_ERATIO;
-    if (R < 0 || R > (ratio >= 8 ? kMaxLongRows : kMaxRows) || num_pages < 0 || num_pages > kMaxPages ||
+    if (R < 0 || R > (ratio >= 64 ? kMaxLongRows : kMaxRows) || num_pages < 0 || num_pages > kMaxPages ||
         max_pos <= 0)
         return KVQ_EINVAL;
     if (R == 0) return KVQ_OK;

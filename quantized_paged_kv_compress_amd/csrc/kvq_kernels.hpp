@@ -47,76 +47,40 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void store_kernel(
     quantize_store_row<L>(pool, static_cast<uint32_t>(slot), v, lane);
 }
 
-// ------------------------------------------------------------------ short-window compressor
-// Ratio r <= 4: one wavefront per output row; the r window rows of kv and score are all
-// loaded up front (4r 16-byte loads per lane in flight), so the per-channel maximum is
-// exact and the weights exp(s - max) need no online rescaling.  The loads and the cos/sin
-// gather are issued before the slot / position checks (which only gate the stores), so a
-// wavefront waits on memory once.  Pooling is float64 (pool_* in kvq_device.hpp); ratio 1
-// is the identity and skips the scores.
-template <Layout L, int kRatio>
-__global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_short_kernel(
-    uint8_t* __restrict__ pool, int64_t nslots, const float* __restrict__ kv,
-    const float* __restrict__ score, int64_t ld, const int32_t* __restrict__ pos,
-    const float* __restrict__ cos_sin, int64_t max_pos, const int32_t* __restrict__ slots,
-    int64_t R) {
-    static_assert(kRatio >= 1 && kRatio <= 4, "short window");
+// ------------------------------------------------------------------ ratio 1 (c1)
+// A one-row window pools to the row itself: round the fp32 kv row to bf16, RoPE, quantise,
+// store (scores are not read).  One wavefront per row, 4 rows per workgroup; rows past R
+// (last block) read row R-1 and store nothing.
+template <Layout L>
+__global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_c1_kernel(
+    uint8_t* __restrict__ pool, int64_t nslots, const float* __restrict__ kv, int64_t ld,
+    const int32_t* __restrict__ pos, const float* __restrict__ cos_sin, int64_t max_pos,
+    const int32_t* __restrict__ slots, int64_t R) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t i_raw = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave_id();
-    const int64_t i = i_raw < R ? i_raw : R - 1;  // rows past R (last block) read row R-1, store nothing
-
-    const int64_t base = i * kRatio * ld;
-    float x[kRatio][8];
-    float s[kRatio > 1 ? kRatio : 1][8];
-#pragma unroll
-    for (int j = 0; j < kRatio; ++j) {
-        load_row_f32(kv + base + j * ld, lane, x[j]);
-        if constexpr (kRatio > 1) load_row_f32(score + base + j * ld, lane, s[j]);
-    }
+    const int64_t i = i_raw < R ? i_raw : R - 1;
+    float v[8];
+    load_row_f32(kv + i * ld, lane, v);
     const int32_t slot = slots[i];
     const int32_t p = pos[i];
     const bool valid = i_raw < R && slot >= 0 && slot < nslots && p >= 0 && p < max_pos;
     RopeCS cs;
     rope_load_cs(cos_sin + static_cast<int64_t>(valid ? p : 0) * kRopeDim, lane, cs);
-
-    float v[8];
-    if constexpr (kRatio == 1) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = round_bf16(x[0][e]);
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float m = s[0][e];
-#pragma unroll
-            for (int j = 1; j < kRatio; ++j) m = fmaxf(m, s[j][e]);
-            const double md = m;
-            double den = 0.0, num = 0.0;
-#pragma unroll
-            for (int j = 0; j < kRatio; ++j) {
-                const double w = exp_f64(static_cast<double>(s[j][e]) - md);
-                den += w;
-                num = __builtin_fma(w, static_cast<double>(x[j][e]), num);
-            }
-            v[e] = pool_result(den, num);
-        }
-    }
+    for (int e = 0; e < 8; ++e) v[e] = round_bf16(v[e]);
     rope_apply(v, cs, lane);
     if (!valid) return;
     quantize_store_row<L>(pool, static_cast<uint32_t>(slot), v, lane);
 }
 
-// ------------------------------------------------------------------ long-window compressor
-// Large ratios (8..128): one workgroup of kWaves wavefronts per output row.  The window is
-// cut into chunks of kChunk rows dealt round-robin to the wavefronts (wavefront w folds
-// chunks w, w + kWaves, ...), so the whole workgroup sweeps its window front to back
-// together -- measured on MI355X about 3 % faster than giving each wavefront a contiguous
-// slice.  Each wavefront double-buffers its chunks (the next chunk's loads are in flight
-// while the current one is folded in; a share of at most four chunks is loaded whole
-// before folding, which measured faster at ratio 64) and keeps a float64 online softmax
-// state per channel (the online form of the vLLM page's section 2; PoolF64).  Every
-// wavefront starts from the same reference, the window's first score row, so the partial
-// states normally merge by plain addition.  Wavefronts 1.. write their states to LDS and
-// wavefront 0 merges them, rounds, rotates, quantises and stores the row.
+// ------------------------------------------------------------------ window per wavefront
+// Ratios 2..32: one wavefront per output row, 4 rows per workgroup, no cross-wavefront
+// merge (measured on MI355X faster than a workgroup per row up to ratio 32).  The wavefront keeps kDepth - 1 chunks of kChunk window rows in flight while it
+// folds the current one into its float64 online softmax state (PoolF64, exp_tab), with
+// the window's first score row as the reference; ratios up to 4 are a single chunk (all
+// loads issued at once).  The loads and the cos/sin gather are issued before the slot /
+// position checks, which only gate the store; rows past R (last block) read row R-1 and
+// store nothing.
 template <int kChunk>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ kv, const float* __restrict__ score,
                                            int64_t base, int64_t ld, int lane, float (&x)[kChunk][8],
@@ -128,6 +92,63 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ kv, const f
     }
 }
 
+template <Layout L, int kRatio, int kChunk, int kDepth>
+__global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_wave_kernel(
+    uint8_t* __restrict__ pool, int64_t nslots, const float* __restrict__ kv,
+    const float* __restrict__ score, int64_t ld, const int32_t* __restrict__ pos,
+    const float* __restrict__ cos_sin, int64_t max_pos, const int32_t* __restrict__ slots,
+    int64_t R) {
+    constexpr int kChunks = kRatio / kChunk;
+    static_assert(kRatio % kChunk == 0 && kDepth >= 2, "window split");
+    __shared__ double tab[256];
+    ExpTableCopy<kWave * kRowsPerBlock> tcopy;
+    tcopy.fetch();
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t i_raw = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave_id();
+    const int64_t i = i_raw < R ? i_raw : R - 1;
+    const int64_t base = i * kRatio * ld;
+    const int64_t step = static_cast<int64_t>(kChunk) * ld;
+    float x[kDepth][kChunk][8], sc[kDepth][kChunk][8];
+#pragma unroll
+    for (int c = 0; c < kDepth - 1 && c < kChunks; ++c)
+        load_chunk<kChunk>(kv, score, base + c * step, ld, lane, x[c], sc[c]);
+    const int32_t slot = slots[i];
+    const int32_t p = pos[i];
+    const bool valid = i_raw < R && slot >= 0 && slot < nslots && p >= 0 && p < max_pos;
+    RopeCS cs;
+    rope_load_cs(cos_sin + static_cast<int64_t>(valid ? p : 0) * kRopeDim, lane, cs);
+    tcopy.put(tab);
+    __syncthreads();  // the exp table is in LDS
+
+    PoolF64 st;
+    pool_init(st, sc[0][0]);
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        if (c + kDepth - 1 < kChunks)
+            load_chunk<kChunk>(kv, score, base + (c + kDepth - 1) * step, ld, lane, x[(c + kDepth - 1) % kDepth],
+                               sc[(c + kDepth - 1) % kDepth]);
+        pool_fold<kChunk>(st, x[c % kDepth], sc[c % kDepth], tab);
+    }
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = pool_result(st.l[e], st.acc[e]);
+    rope_apply(v, cs, lane);
+    if (!valid) return;
+    quantize_store_row<L>(pool, static_cast<uint32_t>(slot), v, lane);
+}
+
+// ------------------------------------------------------------------ long-window compressor
+// Large ratios (8..128): one workgroup of kWaves wavefronts per output row.  The window is
+// cut into chunks of kChunk rows dealt round-robin to the wavefronts (wavefront w folds
+// chunks w, w + kWaves, ...), so the whole workgroup sweeps its window front to back
+// together.  Each wavefront keeps kDepth - 1 chunks in flight while it folds the current
+// one into a float64 online softmax state per channel (the online form of the vLLM page's
+// section 2; PoolF64, weights from exp_tab).  Every wavefront starts from the same
+// reference, the window's first score row, so the partial states normally merge by plain
+// addition.  Wavefronts 1.. write their states to LDS and wavefront 0 merges them, rounds,
+// rotates, quantises and stores the row.  Measured on MI355X: ratio 128 is fastest with 4
+// wavefronts, 1-row chunks and 2 chunks in flight, ratio 64 with 2 wavefronts, 2-row
+// chunks and 2 in flight; 8 wavefronts per row run 10-20 % slower with float64 pooling.
 // This lane's 8 channels (two-half mapping) of a channel-indexed row held in LDS.
 __device__ __forceinline__ void load_lds_f32x8(const float* row, int lane, float (&v)[8]) {
 #pragma unroll
@@ -146,23 +167,28 @@ __device__ __forceinline__ void load_lds_f64x8(const double* row, int lane, doub
     }
 }
 
-template <Layout L, int kRatio, int kWaves, int kChunk>
-__global__ __launch_bounds__(kWave * kWaves) void compress_long_kernel(
+// Two wavefronts per SIMD, a 256-register budget (the compiler would otherwise aim for
+// more wavefronts and spill the in-flight chunks).
+template <Layout L, int kRatio, int kWaves, int kChunk, int kDepth>
+__global__ __launch_bounds__(kWave * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void compress_long_kernel(
     uint8_t* __restrict__ pool, int64_t nslots, const float* __restrict__ kv,
     const float* __restrict__ score, int64_t ld, const int32_t* __restrict__ pos,
     const float* __restrict__ cos_sin, int64_t max_pos, const int32_t* __restrict__ slots,
     int64_t R) {
-    constexpr int kChunksPerWave = kRatio / (kWaves * kChunk);
-    static_assert(kRatio % (kWaves * kChunk) == 0 && kChunksPerWave % 2 == 0, "window split");
-    // partial states of wavefronts 1..kWaves-1, channel-indexed
+    constexpr int kChunks = kRatio / (kWaves * kChunk);   // chunks per wavefront
+    static_assert(kRatio % (kWaves * kChunk) == 0 && kChunks >= 1 && kDepth >= 2, "window split");
+    // partial states of wavefronts 1..kWaves-1, channel-indexed; the exp table
     __shared__ __attribute__((aligned(16))) double part_l[kWaves - 1][kHeadDim];
     __shared__ __attribute__((aligned(16))) double part_a[kWaves - 1][kHeadDim];
     __shared__ __attribute__((aligned(16))) float part_r[kWaves - 1][kHeadDim];
+    __shared__ double tab[256];
 
     const int64_t i = blockIdx.x;
     const int32_t slot = slots[i];
     const int32_t p = pos[i];
     if (slot < 0 || slot >= nslots || p < 0 || p >= max_pos) return;  // whole workgroup
+    ExpTableCopy<kWave * kWaves> tcopy;
+    tcopy.fetch();
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = wave_id();
@@ -176,24 +202,18 @@ __global__ __launch_bounds__(kWave * kWaves) void compress_long_kernel(
         load_row_f32(score + row0, lane, ref);
         pool_init(st, ref);
     }
-
-    if constexpr (kChunksPerWave <= 4) {
-        // the wavefront's whole share fits in registers: issue every load, then fold
-        float x[kChunksPerWave][kChunk][8], sc[kChunksPerWave][kChunk][8];
+    float x[kDepth][kChunk][8], sc[kDepth][kChunk][8];
 #pragma unroll
-        for (int c = 0; c < kChunksPerWave; ++c) load_chunk<kChunk>(kv, score, base + c * step, ld, lane, x[c], sc[c]);
+    for (int c = 0; c < kDepth - 1 && c < kChunks; ++c)
+        load_chunk<kChunk>(kv, score, base + c * step, ld, lane, x[c], sc[c]);
+    tcopy.put(tab);
+    __syncthreads();  // the exp table is in LDS
 #pragma unroll
-        for (int c = 0; c < kChunksPerWave; ++c) pool_fold<kChunk>(st, x[c], sc[c]);
-    } else {
-        float xa[kChunk][8], sa[kChunk][8], xb[kChunk][8], sb[kChunk][8];
-        load_chunk<kChunk>(kv, score, base, ld, lane, xa, sa);
-#pragma unroll 1
-        for (int c = 0; c < kChunksPerWave; c += 2) {
-            load_chunk<kChunk>(kv, score, base + (c + 1) * step, ld, lane, xb, sb);
-            pool_fold<kChunk>(st, xa, sa);
-            if (c + 2 < kChunksPerWave) load_chunk<kChunk>(kv, score, base + (c + 2) * step, ld, lane, xa, sa);
-            pool_fold<kChunk>(st, xb, sb);
-        }
+    for (int c = 0; c < kChunks; ++c) {
+        if (c + kDepth - 1 < kChunks)
+            load_chunk<kChunk>(kv, score, base + (c + kDepth - 1) * step, ld, lane, x[(c + kDepth - 1) % kDepth],
+                               sc[(c + kDepth - 1) % kDepth]);
+        pool_fold<kChunk>(st, x[c % kDepth], sc[c % kDepth], tab);
     }
 
     RopeCS cs;
