@@ -90,6 +90,15 @@ int compress_c1(void* pool, int64_t num_pages, const float* kv, int64_t ld, cons
                   num_pages << kvq::kPageBits, kv, ld, pos, cos_sin, max_pos, slots, R);
 }
 
+template <Layout L, int kRatio>
+int compress_short(void* pool, int64_t num_pages, const float* kv, const float* score, int64_t ld,
+                   const int32_t* pos, const float* cos_sin, int64_t max_pos,
+                   const int32_t* slots, int64_t R, void* stream) {
+    return launch(kvq::compress_short_kernel<L, kRatio>, dim3(blocks_for(R, kvq::kRowsPerBlock)),
+                  dim3(kvq::kWave * kvq::kRowsPerBlock), stream, static_cast<uint8_t*>(pool),
+                  num_pages << kvq::kPageBits, kv, score, ld, pos, cos_sin, max_pos, slots, R);
+}
+
 template <Layout L, int kRatio, int kChunk, int kDepth>
 int compress_wave(void* pool, int64_t num_pages, const float* kv, const float* score, int64_t ld,
                   const int32_t* pos, const float* cos_sin, int64_t max_pos,
@@ -117,8 +126,8 @@ int compress_dispatch(int32_t ratio, void* pool, int64_t num_pages, const float*
     const auto* sc = score;
     switch (ratio) {
         case 1: return compress_c1<L>(pool, num_pages, kv, ld, pos, cos_sin, max_pos, slots, R, stream);
-        case 2: return compress_wave<L, 2, 1, 2>(pool, num_pages, kv, sc, ld, pos, cos_sin, max_pos, slots, R, stream);
-        case 4: return compress_wave<L, 4, 2, 2>(pool, num_pages, kv, sc, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 2: return compress_short<L, 2>(pool, num_pages, kv, sc, ld, pos, cos_sin, max_pos, slots, R, stream);
+        case 4: return compress_short<L, 4>(pool, num_pages, kv, sc, ld, pos, cos_sin, max_pos, slots, R, stream);
         case 8: return compress_wave<L, 8, 2, 4>(pool, num_pages, kv, sc, ld, pos, cos_sin, max_pos, slots, R, stream);
         case 16: return compress_wave<L, 16, 2, 4>(pool, num_pages, kv, sc, ld, pos, cos_sin, max_pos, slots, R, stream);
         case 32: return compress_wave<L, 32, 1, 4>(pool, num_pages, kv, sc, ld, pos, cos_sin, max_pos, slots, R, stream);

@@ -73,8 +73,104 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_c1_kernel(
     quantize_store_row<L>(pool, static_cast<uint32_t>(slot), v, lane);
 }
 
+// ------------------------------------------------------------------ short-window compressor
+// Ratios 2 and 4: one wavefront per output row, the whole window loaded up front (4r
+// 16-byte loads per lane in flight), so the per-channel maximum m is exact.  The pooled
+// value is computed in float32 with the hardware exp2 -- as cheap as the loads need --
+// together with a rigorous bound E on its error against the exact value; wherever the one
+// bf16 rounding midpoint next to it lies within E, the channel is recomputed in float64
+// from the registers (exp_f64, IEEE division), so the stored bf16 is always the correctly
+// rounded exact value.  Ingredients of E (u = 2^-24):
+//  - v_exp_f32, measured on gfx950 over every input in [-160, 1]: within 0.79 ulp
+//    (< 2^-23 relative) for normal results; results below 2^-126 are flushed to zero, so
+//    a channel with an exponent argument below -126 is recomputed;
+//  - the argument a = fma(s, L32, -fl(m * L32)) with L32 = fl(log2 e): against the exact
+//    (s - m) log2 e it is off by a term common to the window (it cancels in the ratio)
+//    plus at most (|a| + 2^-23 |m L32|) (u + 2^-26) in log2 units (|L32 / log2 e - 1| <
+//    2^-26), i.e. a relative weight error of ln 2 times that;
+//  - the float32 sums of r positive weights and of r products w x: r u (A + |p| l), with
+//    A = sum of w |x| and l = sum of w;
+//  - the reciprocal and the product that form p = acc / l: 3 u |p|.
+// E = 1.01 ((d_w + r u) (A + |p| l) / l + 3 u |p|), d_w = 2^-23 + the argument term.  The
+// CPU simulation of the workloads' distributions recomputes about 0.06 % of the values.
+template <Layout L, int kRatio>
+__global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_short_kernel(
+    uint8_t* __restrict__ pool, int64_t nslots, const float* __restrict__ kv,
+    const float* __restrict__ score, int64_t ld, const int32_t* __restrict__ pos,
+    const float* __restrict__ cos_sin, int64_t max_pos, const int32_t* __restrict__ slots,
+    int64_t R) {
+    static_assert(kRatio == 2 || kRatio == 4, "short window");
+    constexpr float kU = 0x1p-24f;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t i_raw = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave_id();
+    const int64_t i = i_raw < R ? i_raw : R - 1;  // rows past R (last block) read row R-1, store nothing
+
+    const int64_t base = i * kRatio * ld;
+    float x[kRatio][8], s[kRatio][8];
+#pragma unroll
+    for (int j = 0; j < kRatio; ++j) {
+        load_row_f32(kv + base + j * ld, lane, x[j]);
+        load_row_f32(score + base + j * ld, lane, s[j]);
+    }
+    const int32_t slot = slots[i];
+    const int32_t p = pos[i];
+    const bool valid = i_raw < R && slot >= 0 && slot < nslots && p >= 0 && p < max_pos;
+    RopeCS cs;
+    rope_load_cs(cos_sin + static_cast<int64_t>(valid ? p : 0) * kRopeDim, lane, cs);
+
+    float v[8], mx[8];
+    uint32_t redo = 0;  // bit e: channel e is recomputed in float64
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float m = s[0][e];
+#pragma unroll
+        for (int j = 1; j < kRatio; ++j) m = fmaxf(m, s[j][e]);
+        mx[e] = m;
+        const float mL = m * kLog2e;
+        float l = 0.0f, acc = 0.0f, A = 0.0f, amin = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kRatio; ++j) {
+            const float a = __builtin_fmaf(s[j][e], kLog2e, -mL);
+            const float w = __builtin_amdgcn_exp2f(a);
+            l += w;
+            acc = __builtin_fmaf(w, x[j][e], acc);
+            A = __builtin_fmaf(w, fabsf(x[j][e]), A);
+            amin = fminf(amin, a);
+        }
+        const float rl = __builtin_amdgcn_rcpf(l);
+        const float pc = acc * rl;
+        const float ap = fabsf(pc);
+        const float dw = 0x1p-23f + (0x1p-23f * fabsf(mL) - amin) * (0.6931472f * 1.25f * kU);
+        const float E = 1.01f * ((dw + kRatio * kU) * __builtin_fmaf(ap, l, A) * rl + 3.0f * kU * ap);
+        const float mid = __uint_as_float((__float_as_uint(pc) & 0xFFFF0000u) | 0x8000u);
+        const bool certain = fabsf(pc - mid) > E && E < ap * 0x1p-10f && ap >= 0x1p-100f &&
+                             amin >= -126.0f && fabsf(mL) < 0x1p20f;
+        v[e] = round_bf16(pc);
+        redo |= certain ? 0u : (1u << e);
+    }
+    if (redo) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (redo & (1u << e)) {
+                const double md = mx[e];
+                double den = 0.0, num = 0.0;
+#pragma unroll
+                for (int j = 0; j < kRatio; ++j) {
+                    const double w = exp_f64(static_cast<double>(s[j][e]) - md);
+                    den += w;
+                    num = __builtin_fma(w, static_cast<double>(x[j][e]), num);
+                }
+                v[e] = pool_result(den, num);
+            }
+        }
+    }
+    rope_apply(v, cs, lane);
+    if (!valid) return;
+    quantize_store_row<L>(pool, static_cast<uint32_t>(slot), v, lane);
+}
+
 // ------------------------------------------------------------------ window per wavefront
-// Ratios 2..32: one wavefront per output row, 4 rows per workgroup, no cross-wavefront
+// Ratios 8..32: one wavefront per output row, 4 rows per workgroup, no cross-wavefront
 // merge (measured on MI355X faster than a workgroup per row up to ratio 32).  The wavefront keeps kDepth - 1 chunks of kChunk window rows in flight while it
 // folds the current one into its float64 online softmax state (PoolF64, exp_tab), with
 // the window's first score row as the reference; ratios up to 4 are a single chunk (all
