@@ -70,11 +70,17 @@ MUTATIONS = [
     ("dequant scale rows 16 bytes apart", "const uint8_t* scale = pg + kPageRows * cr + r * sr;",
      "const uint8_t* scale = pg + kPageRows * cr + r * 16;", ["dequant_fp4", "dequant_slots"]),
     ("translate maps unknown full slots to 0", "? table[f] : -1;", "? table[f] : 0;", ["translate"]),
+    ("rope evaluated in double", "float a = x1 * c, b = x2 * s, d = x2 * c, e = x1 * s;\n        float o1 = a - b, o2 = d + e;",
+     "double a = (double)x1 * c, b = (double)x2 * s, d = (double)x2 * c, e = (double)x1 * s;\n"
+     "        double o1 = a - b, o2 = d + e;", ["rope_order"]),
+    ("rope with fused multiply-add", "float o1 = a - b, o2 = d + e;",
+     "float o1 = fmaf(x1, c, -b), o2 = fmaf(x2, c, e); (void)a; (void)d;", ["rope_order"]),
 ]
 
 PINS = {
     "rope_pairs": lambda o: pins.test_rope_pairs_and_rotation_direction(o),
     "rope_pos0": lambda o: pins.test_rope_position_zero_is_identity(o),
+    "rope_order": lambda o: pins.test_rope_rounding_order_worked_example(o, golden),
     "ue8m0": lambda o: pins.test_ue8m0_exhaustive_bf16_amax(o),
     "v41_worked": lambda o: pins.test_v41_worked_examples(o, golden),
     "e4m3_exhaustive": lambda o: pins.test_e4m3_encode_exhaustive_bf16_inputs(o),

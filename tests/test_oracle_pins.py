@@ -410,6 +410,26 @@ def test_rope_pairs_and_rotation_direction(orc):
                 assert np.all(bf16_vals(out[448:][others]) == 0)
 
 
+def test_rope_rounding_order_worked_example(orc, golden):
+    """Hand-derived row (tests/golden/worked_examples.json, 'rope') where rounding each
+    float32 product and the difference on its own gives a different bf16 than both a
+    float64 evaluation and a fused multiply-add -- pins the rounding order of the rotation,
+    at every pair index."""
+    ex = golden("worked_examples.json")["rope"]
+    for e in ex:
+        x1, x2 = int(e["x1_bf16"], 16), int(e["x2_bf16"], 16)
+        c, s = np.float32(float.fromhex(e["cos"])), np.float32(float.fromhex(e["sin"]))
+        assert int(e["o1_bf16"], 16) not in (int(e["o1_if_float64"], 16), int(e["o1_if_fused"], 16))
+        for i in (0, 17, 31):
+            v = np.zeros(512, np.uint16)
+            v[448 + i], v[480 + i] = x1, x2
+            cs = np.zeros(64, np.float32)
+            cs[i], cs[32 + i] = c, s
+            out = orc.rope_row(v, cs)
+            assert out[448 + i] == int(e["o1_bf16"], 16), (i, hex(out[448 + i]))
+            assert out[480 + i] == int(e["o2_bf16"], 16), (i, hex(out[480 + i]))
+
+
 def test_rope_preserves_pair_norm(orc):
     cs = wl.rope_cos_sin()
     rng = np.random.default_rng(19)
