@@ -145,9 +145,9 @@ def store_configs(kvq, wl, dev, cs, reps=20, calls=50):
 def micro_bench(kvq, wl, dev, cs, layers=61, reps=20, calls=50):
     """Graph-replayed per-launch latency of the kernels in P1's latency table (store,
     store+RoPE, fused K norm+RoPE, c1, c2 at 1/8/64/512 tokens, V41, hot inputs), and the
-    P2 hoisting case:
-    one full->SWA translation reused by `layers` per-layer store+RoPE calls, against a
-    translation inside every layer."""
+    P2 hoisting case: 512 tokens stored into `layers` per-layer pools with one full->SWA
+    translation per step (one store call per layer, or one kv_store_rope_layers launch for
+    all layers) against a translation inside every layer."""
     import numpy as np
     import torch
 
@@ -177,7 +177,8 @@ def micro_bench(kvq, wl, dev, cs, layers=61, reps=20, calls=50):
         for name, fn in fns.items():
             table.setdefault(name, {})[f"bs{bs}"] = round(graph_us(fn, calls, reps), 3)
 
-    # P2: translate once per step vs once per layer, 512 new tokens, `layers` layers
+    # P2: translate once per step vs once per layer; 512 new tokens stored into `layers`
+    # SWA pools, each layer with its own K rows
     n, cap = 512, 4096
     swa_pages = 64
     full = t((rng.permutation(swa_pages * 64)[:n] + 64 * 8).astype(np.int32))
@@ -185,26 +186,101 @@ def micro_bench(kvq, wl, dev, cs, layers=61, reps=20, calls=50):
     tab[64 * 8:64 * 8 + swa_pages * 64] = rng.permutation(swa_pages * 64).astype(np.int32)
     tab = t(tab)
     buf = torch.empty(cap, dtype=torch.int32, device=dev)
-    k = t(wl.bf16_bits(rng.standard_normal((n, HEAD)).astype(np.float32)))
+    ks = [t(wl.bf16_bits(rng.standard_normal((n, HEAD)).astype(np.float32))) for _ in range(layers)]
     pos = t(rng.integers(0, 65536, n).astype(np.int32))
     pools = [kvq.new_pool(kvq.V41, swa_pages) for _ in range(layers)]
 
-    def hoisted():
-        loc = kvq.kv_translate_slots(tab, full, buf)
-        for p in pools:
-            kvq.kv_store_rope(p, kvq.V41, k, pos, cs, loc)
-
     def per_layer():
-        for p in pools:
+        for p, k in zip(pools, ks):
             loc = kvq.kv_translate_slots(tab, full, buf)
             kvq.kv_store_rope(p, kvq.V41, k, pos, cs, loc)
 
+    def hoisted_calls():
+        loc = kvq.kv_translate_slots(tab, full, buf)
+        for p, k in zip(pools, ks):
+            kvq.kv_store_rope(p, kvq.V41, k, pos, cs, loc)
+
+    def hoisted_one_launch():
+        loc = kvq.kv_translate_slots(tab, full, buf)
+        kvq.kv_store_rope_layers(pools, kvq.V41, ks, pos, cs, loc)
+
+    # the one-launch store's own duration (dispatch-recorded events), inputs cold: a 512 MiB
+    # write between repetitions evicts the 32 MB of K rows from the caches
+    alg = layers * n * (2 * HEAD + 528) + n * (4 + 4 + 256)
+    flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+    loc = kvq.kv_translate_slots(tab, full, buf)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(); e1.record()
+    kern = []
+    for r in range(reps + 3):
+        flush.fill_(float(r))
+        kvq.profile_next_launch(e0, e1)
+        kvq.kv_store_rope_layers(pools, kvq.V41, ks, pos, cs, loc)
+        e1.synchronize()
+        if r >= 3:
+            kern.append(e0.elapsed_time(e1) * 1e3)
+    del flush
+    kus = float(np.median(kern))
     step = {"layers": layers, "tokens": n,
-            "hoisted_us_per_step": round(graph_us(hoisted, 1, reps), 2),
-            "per_layer_translate_us_per_step": round(graph_us(per_layer, 1, reps), 2)}
+            "per_layer_translate_us_per_step": round(graph_us(per_layer, 1, reps), 2),
+            "hoisted_per_layer_calls_us_per_step": round(graph_us(hoisted_calls, 1, reps), 2),
+            "hoisted_one_launch_us_per_step": round(graph_us(hoisted_one_launch, 1, reps), 2),
+            "one_launch_kernel_cold": {"us": round(kus, 2), "alg_bytes": alg,
+                                       "GB/s": round(alg / (kus * 1e-6) / 1e9, 1),
+                                       "frac_of_peak": round(alg / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+            "note": "graph-replayed steps read hot inputs (32 MB of K rows stay in the 256 MB "
+                    "last-level cache); the kernel line reads cold inputs"}
     return {"method": f"HIP graph of {calls} back-to-back launches, median of {reps} replays, "
                       "per-launch microseconds, V41, hot inputs",
             "latency_us": table, "swa_hoisting": step}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the CPU-baseline record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def mixed_graph(kvq, m, cs, reps=20):
+    """The mixed FP4 step (translate -> ratio-4 compress at the translated slots -> dequant
+    of the touched pages) captured as one HIP graph and replayed; each replay is timed by
+    stream events around it, with a 512 MiB write before it so that its inputs are cold."""
+    import numpy as np
+    import torch
+
+    def seq():
+        loc = kvq.kv_translate_slots(m["table"], m["full"], m["loc"])
+        kvq.kv_compress_store(m["pool"], kvq.V41_FP4, m["kv"], m["sc"], 4, m["pos"], cs, loc)
+        kvq.kv_dequant(m["pool"], kvq.V41_FP4, m["page_ids"], m["ws"])
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        seq()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        seq()
+    flush = torch.empty(1 << 27, dtype=torch.float32, device=m["kv"].device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for r in range(reps + 3):
+        flush.fill_(float(r))
+        e0.record()
+        g.replay()
+        e1.record()
+        e1.synchronize()
+        if r >= 3:
+            ts.append(e0.elapsed_time(e1) * 1e3)
+    del flush
+    return float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
 
 
 def device_facts(torch):
@@ -586,19 +662,18 @@ def main():
         oracle.lib()
         all_threads = oracle.num_threads()
 
-    def best_of_two(fn):
-        """Seconds of the faster of two runs of fn (the oracle on the same inputs)."""
-        best = None
-        for _ in range(2):
+    def median_of_three(fn):
+        """Median seconds of three runs of fn (the oracle on the same inputs)."""
+        ts = []
+        for _ in range(3):
             t = time.perf_counter()
             fn()
-            dt = time.perf_counter() - t
-            best = dt if best is None else min(best, dt)
-        return best
+            ts.append(time.perf_counter() - t)
+        return sorted(ts)[1]
 
     def oracle_one_thread(fn, rows, key):
         oracle.set_num_threads(1)
-        cpu_1t[key] = (rows, best_of_two(fn))
+        cpu_1t[key] = (rows, median_of_three(fn))
         oracle.set_num_threads(all_threads)
     for name, seed, ratio in (("c4a", 3, 4), ("c128a", 4, 128)):
         R = 16384
@@ -616,8 +691,8 @@ def main():
             if orc_pool is not None:   # CPU baseline: the oracle on the same rows, chunk by chunk
                 pos_c = np.ascontiguousarray(meta["pos"][i0:i0 + n])
                 slots_c = np.ascontiguousarray(meta["slots"][i0:i0 + n])
-                t_orc += best_of_two(lambda: oracle.kv_compress_store(oracle.V41, orc_pool, a, b, ratio,
-                                                                      pos_c, cs_host, slots_c))
+                t_orc += median_of_three(lambda: oracle.kv_compress_store(oracle.V41, orc_pool, a, b, ratio,
+                                                                          pos_c, cs_host, slots_c))
                 if i0 == 0:
                     scratch = oracle.new_pool(oracle.V41, meta["num_pages"])
                     oracle_one_thread(lambda: oracle.kv_compress_store(
@@ -741,6 +816,14 @@ def main():
             kernels[n]["rows/s"] = round(rows[n] / (avg_ms[n] * 1e-3), 1)
     rows_per_step = sum(rows.values())
     dom = "compress_c128a"
+    mixed_alg = alg["translate"] + alg["compress_mixed_fp4"] + alg["dequant_fp4"]
+    g_us, g_p10, g_p90 = mixed_graph(kvq, m, cs)
+    mixed_graph_line = {"us": round(g_us, 2), "us_p10": round(g_p10, 2), "us_p90": round(g_p90, 2),
+                  "alg_bytes": mixed_alg, "GB/s": round(mixed_alg / (g_us * 1e-6) / 1e9, 1),
+                  "frac_of_peak": round(mixed_alg / (g_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                  "method": "translate + compress + dequant replayed as one HIP graph, cold inputs, "
+                            "median of 20 replays timed by stream events around each"}
+    log(f"mixed step as one graph: {mixed_graph_line['us']} us, {mixed_graph_line['frac_of_peak']} of peak")
     traffic = read_traffic(alg[dom])
 
     micro = nxt = stores = None
@@ -762,15 +845,15 @@ def main():
                                      loc_h[: mx["R"]].copy())
             oracle.kv_dequant(oracle.V41_FP4, pool, mx["page_ids"])
 
-        t_mixed = best_of_two(mixed_step)
+        t_mixed = median_of_three(mixed_step)
         oracle_one_thread(mixed_step, m["R"], "mixed")
         cpu_step = t_mixed + cpu_rows_t["c4a"] + cpu_rows_t["c128a"]
         # single thread, projected to the whole step from the timed samples
         step_1t = cpu_1t["mixed"][1] + sum(cpu_1t[k][1] * 16384 / cpu_1t[k][0] for k in ("c4a", "c128a"))
         cpu = {"value": round(rows_per_step / cpu_step, 1), "unit": "rows/s",
-               "cores": oracle.num_threads(), "kind": "oracle",
+               "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
                "sample": ("the whole step: every row of the mixed FP4 step, C4A and C128A, each part "
-                          "timed twice on the same inputs and the faster run kept, OpenMP over rows; "
+                          "timed three times on the same inputs and the median kept, OpenMP over rows; "
                           "input generation excluded (C128A timed chunk by chunk as its inputs are "
                           "generated)"),
                "seconds": {"mixed_fp4": round(t_mixed, 3), "c4a": round(cpu_rows_t["c4a"], 3),
@@ -778,7 +861,7 @@ def main():
                "single_thread": {
                    "value": round(rows_per_step / step_1t, 1), "unit": "rows/s", "cores": 1,
                    "sample": ("one thread on the whole mixed FP4 step, all 16,384 C4A rows and the "
-                              f"first {cpu_1t['c128a'][0]} C128A rows (faster of two runs each), "
+                              f"first {cpu_1t['c128a'][0]} C128A rows (median of three runs each), "
                               "projected to the whole step"),
                    "seconds": {k: round(v[1], 3) for k, v in cpu_1t.items()}}}
         log(f"cpu oracle: {cpu['value']} rows/s on {cpu['cores']} threads ({cpu_step:.2f} s per step)")
@@ -814,7 +897,9 @@ def main():
             "traffic": None if traffic is None else round(traffic["bytes"]),
         },
         "cpu_baseline": cpu,
+        "library_build_id": kvq.load_library().kvq_build_id().decode(),
         "device": device_facts(torch),
+        "mixed_fp4_step_graph": mixed_graph_line,
         "kernels": kernels,
         "kernel_timing": ("us: HIP events recorded by the kernel's own dispatch (hipExtLaunchKernel), "
                           "mean over the timed steps for compress_c4a and compress_c128a, and over "

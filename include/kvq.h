@@ -134,6 +134,28 @@ int kv_store_rope(int32_t layout, void* pool, int64_t num_pages, const uint16_t*
                   int64_t ld, const int32_t* pos, const float* cos_sin, int64_t max_pos,
                   const int32_t* slots, int64_t n, void* stream);
 
+/* kv_store_rope_layers -- kv_store_rope for L layers at once, for the hoisted per-step
+ * slot translation of [P2] (sections 1-2, "why this is a good optimisation" items 1-2:
+ * translate out_cache_loc once per step, then every layer's store reuses the result).
+ * For every layer l < L and row i < n: row i of that layer's K (k_layers[l] + i*ld) is
+ * rotated at pos[i] and stored at slots[i] of that layer's pool (pools[l]), exactly as
+ * kv_store_rope does.  One kernel launch covers up to KVQ_MAX_LAYERS layers (more layers
+ * take further launches on the same stream); the positions, slots and cos/sin rows are
+ * shared by all layers.
+ *   pools      HOST array of L device pool pointers, each num_pages pages of `layout`,
+ *              16-byte aligned; read during the call only (the pointers travel as
+ *              kernel arguments, so a graph capture keeps them)
+ *   k_layers   HOST array of L device bf16 K pointers (same ld for every layer), 16-byte
+ *              aligned
+ *   L          number of layers, >= 1; n * L <= KVQ_MAX_ROWS
+ * Other arguments, skipping rules and errors as kv_store_rope.  Distinct layers must not
+ * share a pool (rows of different layers would race). */
+#define KVQ_MAX_LAYERS 64
+int kv_store_rope_layers(int32_t layout, void* const* pools, int64_t num_pages,
+                         const uint16_t* const* k_layers, int64_t ld, int32_t L, const int32_t* pos,
+                         const float* cos_sin, int64_t max_pos, const int32_t* slots, int64_t n,
+                         void* stream);
+
 /* kv_store_norm_rope -- the fused "K norm + RoPE" store of [P1]'s latency table.  The
  * page gives no formula; this library reads it as RMS normalisation of the whole row with
  * a per-channel weight, y_c = bf16((x_c * w_c) / sqrt(mean_c(x_c^2) + eps)), evaluated in

@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "V41", "V41_FP4", "KVQError", "load_library", "profile_next_launch", "bytes_per_token", "page_bytes",
-    "code_row_bytes", "scale_row_bytes", "new_pool", "kv_store", "kv_store_rope", "kv_store_norm_rope",
+    "code_row_bytes", "scale_row_bytes", "new_pool", "kv_store", "kv_store_rope", "kv_store_rope_layers", "kv_store_norm_rope",
     "kv_compress_store", "kv_compress_state_update", "new_compress_state", "compress_state_bytes", "kv_dequant", "kv_dequant_slots", "kv_translate_slots", "SUPPORTED_RATIOS",
 ]
 
@@ -69,6 +69,7 @@ def load_library() -> ctypes.CDLL:
         "kv_store": [i32, vp, i64, vp, i64, vp, i64, vp],
         "kv_store_rope": [i32, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp],
         "kv_store_norm_rope": [i32, vp, i64, vp, i64, vp, ctypes.c_float, vp, vp, i64, vp, i64, vp],
+        "kv_store_rope_layers": [i32, vp, i64, vp, i64, i32, vp, vp, i64, vp, i64, vp],
         "kv_compress_store": [i32, vp, i64, vp, vp, i64, i32, vp, vp, i64, vp, i64, vp],
         "kv_compress_state_update": [i32, vp, i64, vp, vp, i64, i32, vp, vp, vp, i64, vp, vp, i64, vp,
                                      i64, vp],
@@ -198,6 +199,37 @@ def kv_store_rope(pool, layout, k, pos, cos_sin, slots, stream=None):
     _raise("kv_store_rope", load_library().kv_store_rope(
         layout, _ptr(pool), num_pages, _ptr(k), ld, _ptr(pos), _ptr(cos_sin), cos_sin.shape[0],
         _ptr(slots), n, _stream(stream)))
+
+
+def kv_store_rope_layers(pools, layout, ks, pos, cos_sin, slots, stream=None):
+    """kv_store_rope for every layer l: row i of ks[l] is rotated at pos[i] and stored at
+    slots[i] of pools[l].  pools and ks are equal-length sequences; every K tensor has the
+    same row stride.  One launch per 64 layers."""
+    pools, ks = list(pools), list(ks)
+    if not pools or len(pools) != len(ks):
+        raise ValueError("pools and ks: one pool and one K tensor per layer")
+    num_pages = _pool(pools[0], layout)
+    for p in pools[1:]:
+        if _pool(p, layout) != num_pages:
+            raise ValueError("pools: every layer's pool has the same number of pages")
+    ld = _rows(_dev(ks[0], "ks[0]", _BF16), "ks[0]")
+    for j, k in enumerate(ks[1:], 1):
+        if _rows(_dev(k, f"ks[{j}]", _BF16), f"ks[{j}]") != ld:
+            raise ValueError("ks: every layer's K has the same row stride")
+    _vec(pos, "pos")
+    _vec(slots, "slots")
+    _dev(cos_sin, "cos_sin", _F32)
+    if not cos_sin.is_contiguous() or cos_sin.dim() != 2 or cos_sin.shape[1] != ROPE_DIM:
+        raise ValueError("cos_sin: need a contiguous fp32 [max_pos, 64] tensor")
+    n = slots.numel()
+    if pos.numel() != n or any(k.shape[0] < n for k in ks):
+        raise ValueError("ks / pos / slots sizes disagree")
+    L = len(pools)
+    pool_ptrs = (ctypes.c_void_p * L)(*[p.data_ptr() for p in pools])
+    k_ptrs = (ctypes.c_void_p * L)(*[k.data_ptr() for k in ks])
+    _raise("kv_store_rope_layers", load_library().kv_store_rope_layers(
+        layout, pool_ptrs, num_pages, k_ptrs, ld, L, _ptr(pos), _ptr(cos_sin), cos_sin.shape[0], _ptr(slots), n,
+        _stream(stream)))
 
 
 def kv_store_norm_rope(pool, layout, k, weight, eps, pos, cos_sin, slots, stream=None):

@@ -222,6 +222,37 @@ int kv_store_rope(int32_t layout, void* pool, int64_t num_pages, const uint16_t*
                         stream);
 }
 
+int kv_store_rope_layers(int32_t layout, void* const* pools, int64_t num_pages, const uint16_t* const* k_layers,
+                         int64_t ld, int32_t L, const int32_t* pos, const float* cos_sin, int64_t max_pos,
+                         const int32_t* slots, int64_t n, void* stream) {
+    static_assert(kvq::kMaxLayers == KVQ_MAX_LAYERS, "layer capacity");
+    if (!known_layout(layout)) return KVQ_ELAYOUT;
+    if (L < 1 || n < 0 || n > kMaxRows / L || num_pages < 0 || num_pages > kMaxPages || max_pos <= 0)
+        return KVQ_EINVAL;
+    if (n == 0) return KVQ_OK;
+    if (!pools || !k_layers || !pos || !cos_sin || !slots || !aligned16(cos_sin)) return KVQ_EINVAL;
+    if (ld < kvq::kHeadDim || ld % 8 != 0) return KVQ_EINVAL;
+    for (int32_t l = 0; l < L; ++l)
+        if (!pools[l] || !k_layers[l] || !aligned16(pools[l]) || !aligned16(k_layers[l])) return KVQ_EINVAL;
+    const int64_t nslots = num_pages << kvq::kPageBits;
+    for (int32_t l0 = 0; l0 < L; l0 += kvq::kMaxLayers) {
+        const int32_t cnt = L - l0 < kvq::kMaxLayers ? L - l0 : kvq::kMaxLayers;
+        kvq::LayerPtrs ptrs = {};
+        for (int32_t j = 0; j < cnt; ++j) {
+            ptrs.pool[j] = static_cast<uint8_t*>(pools[l0 + j]);
+            ptrs.k[j] = k_layers[l0 + j];
+        }
+        const dim3 grid(blocks_for(n * cnt, kvq::kRowsPerBlock)), block(kvq::kWave * kvq::kRowsPerBlock);
+        const int st = layout == KVQ_LAYOUT_V41
+                           ? launch(kvq::store_layers_kernel<Layout::V41>, grid, block, stream, ptrs, cnt, nslots,
+                                    ld, pos, cos_sin, max_pos, slots, n)
+                           : launch(kvq::store_layers_kernel<Layout::V41_FP4>, grid, block, stream, ptrs, cnt,
+                                    nslots, ld, pos, cos_sin, max_pos, slots, n);
+        if (st != KVQ_OK) return st;
+    }
+    return KVQ_OK;
+}
+
 int kv_store_norm_rope(int32_t layout, void* pool, int64_t num_pages, const uint16_t* k, int64_t ld,
                        const uint16_t* weight, float eps, const int32_t* pos, const float* cos_sin,
                        int64_t max_pos, const int32_t* slots, int64_t n, void* stream) {

@@ -21,8 +21,9 @@ __device__ __forceinline__ int wave_id() {
 }
 
 // ------------------------------------------------------------------ store / store+RoPE
-// One wavefront per bf16 row: two 8-byte loads per lane, optional RMS norm (kNorm, always
-// followed by RoPE), optional RoPE, quantise, store.
+// One wavefront per bf16 row: two 8-byte loads per lane (issued before the slot and
+// position checks, which only gate the store), optional RMS norm (kNorm, always followed
+// by RoPE), optional RoPE, quantise, store.
 template <Layout L, bool kRope, bool kNorm>
 __global__ __launch_bounds__(kWave * kRowsPerBlock) void store_kernel(
     uint8_t* __restrict__ pool, int64_t nslots, const uint16_t* __restrict__ k, int64_t ld,
@@ -32,19 +33,57 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void store_kernel(
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t i = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave_id();
     if (i >= n) return;
+    float v[8];
+    load_row_bf16(k + i * ld, lane, v);  // issued before the checks, which only gate the store
     const int32_t slot = slots[i];
-    if (slot < 0 || slot >= nslots) return;
     RopeCS cs;
+    bool valid = slot >= 0 && slot < nslots;
     if constexpr (kRope) {
         const int32_t p = pos[i];
-        if (p < 0 || p >= max_pos) return;
-        rope_load_cs(cos_sin + static_cast<int64_t>(p) * kRopeDim, lane, cs);
+        valid = valid && p >= 0 && p < max_pos;
+        rope_load_cs(cos_sin + static_cast<int64_t>(valid ? p : 0) * kRopeDim, lane, cs);
     }
-    float v[8];
-    load_row_bf16(k + i * ld, lane, v);
+    if (!valid) return;
     if constexpr (kNorm) rms_norm_row(v, weight, eps, lane);
     if constexpr (kRope) rope_apply(v, cs, lane);
     quantize_store_row<L>(pool, static_cast<uint32_t>(slot), v, lane);
+}
+
+// ------------------------------------------------------------------ store + RoPE, many layers
+// kv_store_rope for up to kMaxLayers layers in one launch: the pool and K pointers of
+// every layer travel by value in the kernel arguments.  Wavefront g handles layer g / n,
+// row g % n, so consecutive wavefronts stream consecutive rows of one layer; the row load
+// is issued before the slot, position and cos/sin loads, which only gate the store.  The
+// positions, slots and cos/sin rows are shared by all layers (after the first layer they
+// come from L2).  Measured on MI355X at 61 layers x 512 tokens, cold: within about 20 %
+// of a memory twin that makes the same loads and stores with no arithmetic; giving a
+// wavefront 2 or 4 layers of one token is no faster.
+constexpr int kMaxLayers = 64;
+
+struct LayerPtrs {
+    uint8_t* pool[kMaxLayers];
+    const uint16_t* k[kMaxLayers];
+};
+
+template <Layout L>
+__global__ __launch_bounds__(kWave * kRowsPerBlock) void store_layers_kernel(
+    LayerPtrs layers, int32_t num_layers, int64_t nslots, int64_t ld, const int32_t* __restrict__ pos,
+    const float* __restrict__ cos_sin, int64_t max_pos, const int32_t* __restrict__ slots, int64_t n) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t g = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave_id();
+    if (g >= n * num_layers) return;
+    const int layer = static_cast<int>(g / n);
+    const int64_t i = g - static_cast<int64_t>(layer) * n;
+    float v[8];
+    load_row_bf16(layers.k[layer] + i * ld, lane, v);
+    const int32_t slot = slots[i];
+    const int32_t p = pos[i];
+    const bool valid = slot >= 0 && slot < nslots && p >= 0 && p < max_pos;
+    RopeCS cs;
+    rope_load_cs(cos_sin + static_cast<int64_t>(valid ? p : 0) * kRopeDim, lane, cs);
+    if (!valid) return;
+    rope_apply(v, cs, lane);
+    quantize_store_row<L>(layers.pool[layer], static_cast<uint32_t>(slot), v, lane);
 }
 
 // ------------------------------------------------------------------ ratio 1 (c1)

@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("kv_store", "kv_store_rope", "kv_store_norm_rope", "kv_compress_store",
                  "kv_compress_state_update", "kv_dequant_slots", "kv_dequant",
-                 "kv_translate_slots", "kvq_bytes_per_token", "kvq_page_bytes",
+                 "kv_translate_slots", "kvq_bytes_per_token", "kvq_page_bytes", "kv_store_rope_layers",
                  "kvq_profile_next_launch"):
         assert want in names
 
@@ -280,3 +280,37 @@ def test_sizes_beyond_one_launch_are_rejected(kvq):
                                    None) == kvq.KVQ_EINVAL
     assert L.kv_dequant(V41, A, 4, B, max_pages + 1, C, None) == kvq.KVQ_EINVAL
     assert L.kv_translate_slots(A, 100, B, 5, C, 1 << 31, None) == kvq.KVQ_EINVAL
+
+
+def test_store_rope_layers_argument_checks(kvq):
+    """Host arrays of (fake, never dereferenced) device pointers: every bad argument is
+    refused before a launch."""
+    L = kvq.load_library()
+    vp = ctypes.c_void_p
+
+    def arr(*xs):
+        return (vp * len(xs))(*xs)
+    pools, ks = arr(A, B, C), arr(B, C, A)
+    ok = dict(layout=V41, pools=pools, num_pages=4, ks=ks, ld=512, L=3, pos=A, cs=B, max_pos=10, slots=C, n=5,
+              stream=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.kv_store_rope_layers(*a.values())
+    assert call(n=0) == kvq.KVQ_OK
+    assert call(layout=5) == kvq.KVQ_ELAYOUT
+    assert call(L=0) == kvq.KVQ_EINVAL
+    assert call(L=-2) == kvq.KVQ_EINVAL
+    assert call(pools=None) == kvq.KVQ_EINVAL
+    assert call(ks=None) == kvq.KVQ_EINVAL
+    assert call(pools=arr(A, None, C)) == kvq.KVQ_EINVAL
+    assert call(pools=arr(A, B + 8, C)) == kvq.KVQ_EINVAL
+    assert call(ks=arr(B, C, A + 2)) == kvq.KVQ_EINVAL
+    assert call(ld=500) == kvq.KVQ_EINVAL
+    assert call(ld=516) == kvq.KVQ_EINVAL
+    assert call(max_pos=0) == kvq.KVQ_EINVAL
+    assert call(pos=None) == kvq.KVQ_EINVAL
+    assert call(cs=B + 4) == kvq.KVQ_EINVAL
+    assert call(n=(1 << 25) // 3 + 1) == kvq.KVQ_EINVAL       # n * L above KVQ_MAX_ROWS
+    assert call(num_pages=(1 << 32) + 1) == kvq.KVQ_EINVAL

@@ -142,6 +142,53 @@ def test_store_exhaustive_encoder_bit_exact(kvq, orc, layout):
                              f"scales {gs[r][:16]} vs {rs[r][:16]}")
 
 
+def every_amax_rows(seed):
+    """One 32-value block per positive finite bf16 amax (0x0001..0x7F7F, 32,639 values) and
+    one all-zero block: the block maximum sits on a rotating channel, with either sign;
+    the other 31 values are bf16 roundings of random fractions of it (random signs), so
+    every block exercises the scale encoder at its amax and the code encoder at that
+    scale.  16 blocks per row."""
+    rng = np.random.default_rng(seed)
+    amax = np.concatenate([np.arange(1, 0x7F80, dtype=np.uint32), [0]]).astype(np.uint32)
+    nb = amax.size
+    av = (amax << 16).view(np.float32)
+    frac = rng.uniform(0, 1, (nb, 32)).astype(np.float32)
+    vals = wl.bf16_bits(frac * av[:, None] * np.where(rng.integers(0, 2, (nb, 32)) == 1, 1, -1))
+    vbits = (vals.astype(np.uint32) << 16).view(np.float32)
+    vals[np.abs(vbits) > av[:, None]] = 0          # rounding up past amax: drop to zero
+    at = np.arange(nb) % 32
+    sign = np.where(rng.integers(0, 2, nb) == 1, 0x8000, 0).astype(np.uint32)
+    vals[np.arange(nb), at] = (amax | sign).astype(np.uint16)
+    pad = (-nb) % 16
+    vals = np.concatenate([vals, np.zeros((pad, 32), np.uint16)])
+    return np.ascontiguousarray(vals.reshape(-1, 512)), nb
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_store_every_bf16_amax_bit_exact(kvq, orc, layout):
+    """The scale byte (ue8m0 from the amax bits for V41, e4m3 RNE of fl32(amax / 6) for
+    V41_FP4) at every positive bf16 amax, and the codes at that scale, bit-exact."""
+    k, nb = every_amax_rows(31 + layout)
+    bits = (k.astype(np.uint32) << 16).view(np.float32).reshape(-1, 32)
+    got_amax = np.abs(bits).max(axis=1).view(np.uint32) >> 16
+    assert set(range(1, 0x7F80)) <= set(got_amax.tolist())
+    n = k.shape[0]
+    num_pages = (n + 63) // 64
+    log(f"[every amax] layout {layout}: {nb} blocks in {n} rows")
+    slots = np.arange(n, dtype=np.int32)
+    pool = kvq.new_pool(layout, num_pages)
+    ref = orc.new_pool(layout, num_pages)
+    kvq.kv_store(pool, layout, to_dev(k), to_dev(slots))
+    orc.kv_store(layout, ref, k, slots)
+    got = to_host(pool)
+    gc, gs = rows_of(got, layout, slots)
+    rc, rs = rows_of(ref, layout, slots)
+    bad = np.argwhere(gs[:, :16] != rs[:, :16])
+    assert bad.size == 0, (f"{len(bad)} scale bytes differ; first row {bad[0][0]} block {bad[0][1]}: "
+                           f"{gs[bad[0][0], bad[0][1]]} vs {rs[bad[0][0], bad[0][1]]}")
+    assert np.array_equal(got, ref)
+
+
 # ------------------------------------------------------------------ store + RoPE
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_store_rope_workload_bit_exact(kvq, orc, cos_sin, cos_sin_dev, layout):
