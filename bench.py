@@ -31,16 +31,11 @@ METRIC = "compressed KV rows/sec + achieved HBM GB/s (% of MI355X peak), C4A & C
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
 HEAD = 512
 PROFILE = os.path.join(ROOT, "profiles", "compress_c128a_v41_pmc.txt")
-KERNEL_SOURCES = ["csrc/kvq_capi.hip", "csrc/kvq_kernels.hpp", "csrc/kvq_device.hpp",
-                  "csrc/kvq_layout.hpp", "_build.py"]
-
-
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "quantized_paged_kv_compress_amd", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
+    """SHA-256 of the library's sources and build flags: the same value libkvq.so reports
+    as kvq_build_id()."""
+    from quantized_paged_kv_compress_amd import _build
+    return _build.source_hash()
 
 
 # ---------------------------------------------------------------- algorithmic bytes
@@ -59,8 +54,9 @@ def bytes_dequant(P, page_bytes):
 
 
 def read_traffic(duration_key_bytes):
-    """HBM bytes per C128A launch from the committed rocprofv3 PMC summary, scaled by
-    the copy-kernel calibration in the same file; None if the kernels changed since."""
+    """HBM bytes per C128A launch from the committed rocprofv3 PMC summary: DRAM read and
+    write sectors (32 bytes each), with FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel
+    calibration in the same file as a cross-check; None if the kernels changed since."""
     if not os.path.exists(PROFILE):
         return None
     kv = {}
@@ -76,9 +72,11 @@ def read_traffic(duration_key_bytes):
         ws = copy_bytes / (float(kv["copy_WRITE_SIZE_KiB_per_dispatch"]) * 1024)
         fetch = float(kv["FETCH_SIZE_KiB_per_dispatch"]) * 1024 * fs
         write = float(kv["WRITE_SIZE_KiB_per_dispatch"]) * 1024 * ws
-        return {"bytes": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
-                "fetch_scale": fs, "write_scale": ws,
-                "ratio_to_algorithmic": (fetch + write) / duration_key_bytes}
+        dram = float(kv["DRAM_read_bytes_per_dispatch"]) + float(kv["DRAM_write_bytes_per_dispatch"])
+        return {"bytes": dram, "dram_read_bytes": float(kv["DRAM_read_bytes_per_dispatch"]),
+                "dram_write_bytes": float(kv["DRAM_write_bytes_per_dispatch"]),
+                "fetch_write_scaled_bytes": fetch + write, "fetch_scale": fs, "write_scale": ws,
+                "ratio_to_algorithmic": dram / duration_key_bytes}
     except (KeyError, ValueError, ZeroDivisionError):
         return None
 
@@ -423,11 +421,14 @@ def ratio_sweep(kvq, wl, dev, cs, kv, sc, c4_pool, c4_slots, reps=5):
 # bench.py reads `traffic` back from the PMC summary.
 PROFILE_RUNS = {
     "trace": "rocprofv3 --kernel-trace --stats -f csv -d $RESULTS/prof_trace -o trace -- "
-             "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-micro",
+             "python3 bench.py --steps 10 --warmup 10 --no-cpu-baseline --no-micro",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d $RESULTS/pmc_fetch -o fetch -- "
              "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-micro",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d $RESULTS/pmc_write -o write -- "
              "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-micro",
+    "dram": "rocprofv3 --pmc TCC_EA0_RDREQ_DRAM_32B_sum TCC_EA0_WRREQ_WRITE_DRAM_32B_sum "
+            "TCC_EA0_RDREQ_128B_sum -f csv -d $RESULTS/pmc_dram -o dram -- "
+            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-micro",
     "next": "rocprofv3 --kernel-trace --stats -f csv -d $RESULTS/prof_next -o next -- "
             "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
 }
@@ -459,24 +460,35 @@ def _find_csv(results, pattern):
     return found[0]
 
 
-def trace_summary(results):
+def trace_summary(results, warmup=10):
     import csv
+    import numpy as np
     rows = list(csv.DictReader(open(_find_csv(results, "prof_trace/**/trace_kernel_stats.csv"))))
+    per = {}
+    for r in csv.DictReader(open(_find_csv(results, "prof_trace/**/trace_kernel_trace.csv"))):
+        name = _short_name(r["Kernel_Name"])
+        if name is not None:
+            per.setdefault(name, []).append((int(r["Start_Timestamp"]),
+                                             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
     lines = [
         "# rocprofv3 kernel-trace summary: one bench step (mixed V41_FP4 step + C4A + C128A), MI355X",
         f"# command: {PROFILE_RUNS['trace']}",
         "# (run from the repository root with TMPDIR=/tmp, RESULTS = the results directory;",
         "#  summarised by: python bench.py --write-profiles $RESULTS)",
-        "# The bench launches every kernel on torch's current stream; 11 launches of each kernel",
-        "# = 1 warmup step + 5 timed steps + 5 steps of the pass that times the kernels not",
-        "# armed in the timed region.",
+        "# The bench launches every kernel on torch's current stream: 30 launches of each step",
+        f"# kernel = {warmup} warmup steps + 10 timed steps + 10 steps of the pass that times the kernels",
+        "# not armed in the timed region.  avg_us covers every launch; after_warmup_us leaves out",
+        f"# the first {warmup} launches of each kernel (the warmup steps, during which the clocks",
+        "# settle), as the bench's own figures do.",
         "",
-        f"{'kernel':<52} {'calls':>5} {'avg_us':>10} {'min_us':>10} {'max_us':>10}",
+        f"{'kernel':<52} {'calls':>5} {'avg_us':>10} {'after_warmup_us':>16} {'min_us':>10} {'max_us':>10}",
     ]
     for r in rows:
         name = _short_name(r["Name"])
         if name is not None:
-            lines.append(f"{name:<52} {int(r['Calls']):>5} {float(r['AverageNs']) / 1e3:>10.2f} "
+            d = [t for _, t in sorted(per.get(name, []))]
+            aw = float(np.mean(d[warmup:])) if len(d) > warmup else float("nan")
+            lines.append(f"{name:<52} {int(r['Calls']):>5} {float(r['AverageNs']) / 1e3:>10.2f} {aw:>16.2f} "
                          f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f}")
     bench_json = os.path.join(results, "bench.json")
     if os.path.exists(bench_json):
@@ -489,12 +501,12 @@ def trace_summary(results):
     return "\n".join(lines) + "\n"
 
 
-def _pmc_per_kernel(path):
+def _pmc_per_kernel(path, counter=None):
     import csv
     agg = {}
     for r in csv.DictReader(open(path)):
         name = _short_name(r["Kernel_Name"])
-        if name is not None:
+        if name is not None and (counter is None or r["Counter_Name"] == counter):
             agg.setdefault(name, []).append((int(r["Grid_Size"]), float(r["Counter_Value"])))
     return agg
 
@@ -511,6 +523,16 @@ def pmc_summary(results):
     ws = (1 << 30) / (copy_write * 1024)
     fk = float(np.mean([v for _, v in f[DOM_KEY]]))
     wk = float(np.mean([v for _, v in w[DOM_KEY]]))
+    dpath = _find_csv(results, "pmc_dram/**/dram_counter_collection.csv")
+    dr = _pmc_per_kernel(dpath, "TCC_EA0_RDREQ_DRAM_32B_sum")
+    dw = _pmc_per_kernel(dpath, "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum")
+    d128 = _pmc_per_kernel(dpath, "TCC_EA0_RDREQ_128B_sum")
+    big_d = {g for g, v in dw[COPY_KEY] if abs(v * 32 - (1 << 30)) < (1 << 24)}
+    copy_dr = float(np.mean([v for g, v in dr[COPY_KEY] if g in big_d])) * 32
+    copy_dw = float(np.mean([v for g, v in dw[COPY_KEY] if g in big_d])) * 32
+    dom_dr = float(np.mean([v for _, v in dr[DOM_KEY]])) * 32
+    dom_dw = float(np.mean([v for _, v in dw[DOM_KEY]])) * 32
+    dom_128 = float(np.mean([v for _, v in d128[DOM_KEY]]))
     lines = [
         "# rocprofv3 PMC summary: HBM traffic per dispatch, MI355X",
         f"# command (pass 1): {PROFILE_RUNS['fetch']}",
@@ -532,6 +554,17 @@ def pmc_summary(results):
         f"copy_FETCH_SIZE_KiB_per_dispatch: {copy_fetch:.3f}",
         f"copy_WRITE_SIZE_KiB_per_dispatch: {copy_write:.3f}",
         "",
+        f"# command (pass 3): {PROFILE_RUNS['dram']}",
+        "# A second, uncalibrated count: DRAM read and write requests in 32-byte sectors",
+        "# (TCC_EA0_RDREQ_DRAM_32B counts a 128-byte request as 4), times 32.  FETCH_SIZE's",
+        "# formula counts every read request that is not 32 bytes as 64 bytes, while gfx950 reads",
+        "# in 128-byte requests (TCC_EA0_RDREQ_128B), which is why the copy calibration finds 2.0.",
+        f"DRAM_read_bytes_per_dispatch: {dom_dr:.0f}",
+        f"DRAM_write_bytes_per_dispatch: {dom_dw:.0f}",
+        f"RDREQ_128B_per_dispatch: {dom_128:.0f}",
+        f"copy_DRAM_read_bytes_per_dispatch: {copy_dr:.0f}",
+        f"copy_DRAM_write_bytes_per_dispatch: {copy_dw:.0f}",
+        "",
         f"# all kernels of the step (raw KiB per dispatch; scaled bytes = fetch*1024*{fs:.1f} + "
         f"write*1024*{ws:.1f}):",
     ]
@@ -542,8 +575,11 @@ def pmc_summary(results):
         fa = float(np.mean([v for _, v in f[k]]))
         wa = float(np.mean([v for _, v in w[k]])) if k in w else 0.0
         tot = fa * 1024 * fs + wa * 1024 * ws
+        dram = (float(np.mean([v for _, v in dr[k]])) + float(np.mean([v for _, v in dw.get(k, [(0, 0.0)])]))) * 32 \
+            if k in dr else float("nan")
         extra = f"  ({tot / alg[k]:.3f} x algorithmic)" if k in alg else ""
-        lines.append(f"#   {k:<48} fetch {fa:>14.1f}  write {wa:>12.1f}  -> {tot / 1e6:>10.2f} MB{extra}")
+        lines.append(f"#   {k:<48} fetch {fa:>14.1f}  write {wa:>12.1f}  -> {tot / 1e6:>10.2f} MB"
+                     f"  (DRAM sectors {dram / 1e6:>10.2f} MB){extra}")
     return "\n".join(lines) + "\n"
 
 
@@ -924,6 +960,9 @@ def main():
     }
     if traffic is not None:
         out["roofline"]["traffic_over_algorithmic"] = round(traffic["ratio_to_algorithmic"], 4)
+        out["roofline"]["traffic_source"] = ("DRAM read + write sectors (TCC_EA0_RDREQ_DRAM_32B, "
+                                             "TCC_EA0_WRREQ_WRITE_DRAM_32B) x 32 B per launch")
+        out["roofline"]["traffic_fetch_write_scaled"] = round(traffic["fetch_write_scaled_bytes"])
     print(json.dumps(out), flush=True)
 
 

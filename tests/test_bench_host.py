@@ -36,6 +36,8 @@ def results(tmp_path):
            ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"],
            [[C128A, 11, 0, 1227020.0, 50, 1219600, 1242440, 0], [C4A, 11, 0, 46840.0, 2, 44510, 52870, 0],
             ["some_other_kernel", 3, 0, 1000.0, 0, 900, 1100, 0]])
+    _write(str(tmp_path / "prof_trace" / "trace_kernel_trace.csv"), ["Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+           [[C128A, 1000 * k, 1000 * k + (1300000 if k < 10 else 1227020)] for k in range(30)])
     # counters in KiB per dispatch: the 1 GiB copy reads half its bytes in FETCH_SIZE
     alg = bench.bytes_compress(16384, 128, 528)
     hdr = ["Kernel_Name", "Grid_Size", "Counter_Value"]
@@ -44,12 +46,22 @@ def results(tmp_path):
             [C4A, 4096, 1000.0]])
     _write(str(tmp_path / "pmc_write" / "write_counter_collection.csv"), hdr,
            [[COPY, 777, 1048576.0], [COPY, 5, 3.0], [C128A, 16384, 0.0], [C4A, 4096, 10.0]])
+    # DRAM sectors of 32 bytes: the copy moves 1 GiB each way; C128A reads 1.01x algorithmic
+    rd, wr, r128 = "TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum", "TCC_EA0_RDREQ_128B_sum"
+    _write(str(tmp_path / "pmc_dram" / "dram_counter_collection.csv"), ["Kernel_Name", "Grid_Size", "Counter_Name",
+                                                                        "Counter_Value"],
+           [[COPY, 777, rd, (1 << 30) / 32], [COPY, 777, wr, (1 << 30) / 32], [COPY, 777, r128, (1 << 30) / 128],
+            [COPY, 5, rd, 10.0], [COPY, 5, wr, 1.0], [COPY, 5, r128, 2.0],
+            [C128A, 16384, rd, alg * 1.01 / 32], [C128A, 16384, wr, 0.0], [C128A, 16384, r128, alg / 128],
+            [C4A, 4096, rd, 100.0], [C4A, 4096, wr, 10.0], [C4A, 4096, r128, 25.0]])
     return str(tmp_path)
 
 
 def test_trace_summary_lists_named_kernels(results):
     text = bench.trace_summary(results)
     assert "compress_long<V41, ratio 128> (C128A)" in text and "1227.02" in text
+    line = [ln for ln in text.splitlines() if ln.startswith("compress_long<V41, ratio 128>")][0]
+    assert line.split()[-4] == "1227.02"           # after the 10 warmup launches
     assert "some_other_kernel" not in text
 
 
@@ -62,6 +74,7 @@ def test_pmc_summary_scales_by_the_copy_and_round_trips(results, tmp_path, monke
     monkeypatch.setattr(bench, "PROFILE", str(prof))
     t = bench.read_traffic(bench.bytes_compress(16384, 128, 528))
     assert t is not None and abs(t["ratio_to_algorithmic"] - 1.01) < 1e-6
+    assert abs(t["fetch_write_scaled_bytes"] / t["bytes"] - 1.0) < 1e-6     # both counts agree
     # a kernel-source change makes the stored counters stale
     prof.write_text(text.replace(bench.kernel_source_hash(), "0" * 64))
     assert bench.read_traffic(bench.bytes_compress(16384, 128, 528)) is None
