@@ -403,14 +403,14 @@ def ratio_sweep(kvq, wl, dev, cs, kv, sc, c4_pool, c4_slots, reps=5):
         ev[1].record()
         ev[1].synchronize()
         us = ev[0].elapsed_time(ev[1]) * 1e3
-        b = S * (r * (HEAD * 8 + 4 + 8) + 2 * (r - 1) * 3 * HEAD * 4 + 4 + 4 + 256 +
+        b = S * (r * (HEAD * 8 + 4 + 8) + 2 * (r - 1) * kvq.compress_state_bytes() + 4 + 4 + 256 +
                  kvq.bytes_per_token(kvq.V41))
         decode[f"r{r}"] = {"sequences": S, "us_per_step": round(us / r, 2), "GB/s": round(b / us / 1e3, 1),
                            "frac_of_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
     return {"method": "HIP events recorded by each launch's own dispatch, median of %d launches "
                       "(decode steps: stream events around one full window); the ratio sweep reads the same 8 GiB "
                       "of cold inputs at every ratio; decode steps fold one row per sequence into "
-                      "its 6 KiB state per call (one full window timed)" % reps,
+                      "its 10 KiB float64 state per call (one full window timed)" % reps,
             "compress_ratio_sweep_v41": sweep, "dequant_slots_c4a_rows": gather,
             "compress_state_decode_v41": decode}
 
