@@ -416,7 +416,7 @@ def ratio_sweep(kvq, wl, dev, cs, kv, sc, c4_pool, c4_slots, reps=5):
 
 
 # ---------------------------------------------------------------- rocprofv3 summaries
-# `python bench.py --write-profiles RESULTS` condenses the CSV output of the
+# `python bench.py --write-profiles RESULTS` condenses the CSV output of the three
 # profiler runs below (written under RESULTS) into the text summaries in profiles/;
 # bench.py reads `traffic` back from the PMC summary.
 PROFILE_RUNS = {
@@ -431,8 +431,6 @@ PROFILE_RUNS = {
             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-micro",
     "next": "rocprofv3 --kernel-trace --stats -f csv -d $RESULTS/prof_next -o next -- "
             "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline",
-    "clock": "rocprofv3 --pmc GRBM_GUI_ACTIVE GRBM_COUNT -f csv -d $RESULTS/pmc_clock -o clock -- "
-             "python3 bench.py --steps 10 --warmup 10 --no-cpu-baseline --no-micro",
 }
 SHORT_NAMES = {
     "compress_long_kernel<(kvq::Layout)1, 128": "compress_long<V41, ratio 128> (C128A)",
@@ -632,43 +630,6 @@ def all_kernels_summary(results):
     return "\n".join(lines) + "\n"
 
 
-def clock_summary(results, warmup=10):
-    """Mean shader clock while each step kernel runs: GRBM_GUI_ACTIVE (busy clocks, summed
-    over the 8 XCDs) / 8 / the dispatch's duration, over the launches after the warmup ones."""
-    import csv
-    import numpy as np
-    per = {}
-    for r in csv.DictReader(open(_find_csv(results, "pmc_clock/**/clock_counter_collection.csv"))):
-        name = _short_name(r["Kernel_Name"])
-        if name is None or r["Counter_Name"] != "GRBM_GUI_ACTIVE":
-            continue
-        dur_ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-        per.setdefault(name, []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"]) / 8 / dur_ns, dur_ns / 1e3))
-    lines = [
-        "# rocprofv3 PMC summary: shader clock while each kernel of the bench step runs, MI355X",
-        f"# command: {PROFILE_RUNS['clock']}",
-        "# (run from the repository root with TMPDIR=/tmp, RESULTS = the results directory;",
-        "#  summarised by: python bench.py --write-profiles $RESULTS)",
-        "# clock = GRBM_GUI_ACTIVE (busy clocks, summed over the 8 XCDs) / 8 / dispatch duration.",
-        "# The counting window is a little longer than the dispatch, so short kernels read high",
-        "# (a few-us kernel can exceed the 2.4 GHz maximum); the profiler serialises dispatches,",
-        f"# so the clock recovers a little between them.  The first {warmup} launches of each kernel",
-        "# (warmup steps) are left out.",
-        "",
-        f"{'kernel':<52} {'launches':>8} {'us_mean':>9} {'GHz_mean':>9} {'GHz_min':>8} {'GHz_max':>8}",
-    ]
-    for name, v in per.items():
-        if name == COPY_KEY:
-            continue
-        v = [x for _, *x in sorted(v)][warmup:]
-        if not v:
-            continue
-        ghz = np.array([x[0] for x in v])
-        us = np.array([x[1] for x in v])
-        lines.append(f"{name:<52} {len(v):>8} {us.mean():>9.2f} {ghz.mean():>9.2f} {ghz.min():>8.2f} {ghz.max():>8.2f}")
-    return "\n".join(lines) + "\n"
-
-
 def write_profiles(results):
     out = os.path.join(ROOT, "profiles")
     os.makedirs(out, exist_ok=True)
@@ -677,8 +638,6 @@ def write_profiles(results):
     import glob
     if glob.glob(os.path.join(results, "prof_next/**/next_kernel_trace.csv"), recursive=True):
         outputs.append(("all_kernels_full_bench_trace.txt", all_kernels_summary(results)))
-    if glob.glob(os.path.join(results, "pmc_clock/**/clock_counter_collection.csv"), recursive=True):
-        outputs.append(("step_kernels_clock_pmc.txt", clock_summary(results)))
     for name, text in outputs:
         with open(os.path.join(out, name), "w") as fh:
             fh.write(text)
