@@ -10,7 +10,8 @@ inputs would not show it.  This test replays the kernel's float32 sequence on th
 with the hardware's error allowances spent adversarially:
   - exp2: any float32 within 0.7827 ulp of 2^a (the largest error measured on gfx950 over
     every input in [-160, 1]), chosen to push the pooled value up, or down;
-  - reciprocal: any float32 within 1 ulp of 1/l, chosen the same way;
+  - reciprocal: any float32 within 1 ulp of 1/l, chosen the same way (0.8818 ulp measured);
+(both allowances are re-measured on the GPU under test by tests/test_gpu_hw_bounds.py)
 and checks, on hard windows (huge score offsets, cancellation, wide spreads, values
 placed next to bf16 midpoints), that wherever the kernel would keep its float32 value,
 that value is within E of the exact pool (evaluated in 64-bit-mantissa long double) and
