@@ -631,6 +631,10 @@ def all_kernels_summary(results):
 
 
 def write_profiles(results):
+    # the summaries are stamped with the hash of the sources in the tree; the library next
+    # to them must have been built from those sources (load_library refuses a stale one)
+    import quantized_paged_kv_compress_amd as kvq
+    kvq.load_library()
     out = os.path.join(ROOT, "profiles")
     os.makedirs(out, exist_ok=True)
     outputs = [("bench_step_kernel_trace.txt", trace_summary(results)),

@@ -438,11 +438,27 @@ __device__ __forceinline__ void rms_norm_row(float (&v)[8], const uint16_t* __re
         v[e] = __uint_as_float(bf16_rne_bits_f64((static_cast<double>(v[e]) * static_cast<double>(w[e])) * r) << 16);
 }
 
+// ---------------------------------------------------------------- stores
+// A store of the output bytes, either plain (the line stays in L2 as dirty data and is
+// written back later) or non-temporal (the `nt` form: streamed out with evict-first
+// priority).  Which one is faster depends on the kernel and was measured per kernel on
+// MI355X: non-temporal pays for kernels that read far more than they write over a long
+// run (the long-window compressors) and for the scattered row writers (the multi-layer
+// store, the token gather); a short kernel whose few MB of output can sit in L2 until it
+// ends (C4A) is faster with plain stores.
+template <bool kNt, typename T>
+__device__ __forceinline__ void put(T* p, T v) {
+    if constexpr (kNt)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
 // ---------------------------------------------------------------- quantise + store
 // Quantise this lane's 8 bf16-valued floats of a row and write its share of the row at
-// `slot` (the caller has checked the slot is inside the pool).  Every lane must call
-// this.
-template <Layout L>
+// `slot` (the caller has checked the slot is inside the pool), with plain or
+// non-temporal stores (kNt).  Every lane must call this.
+template <Layout L, bool kNt = false>
 __device__ __forceinline__ void quantize_store_row(uint8_t* __restrict__ pool, uint32_t slot,
                                                    const float (&v)[8], int lane) {
     using PK = PagedKV<L, kPageBits>;
@@ -473,8 +489,8 @@ __device__ __forceinline__ void quantize_store_row(uint8_t* __restrict__ pool, u
             w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * h + 2] * inv_scale, v[4 * h + 3] * inv_scale, w, true);
             word[h] = static_cast<uint32_t>(w);
         }
-        *reinterpret_cast<uint32_t*>(code_row + 4 * lane) = word[0];
-        *reinterpret_cast<uint32_t*>(code_row + kHalf + 4 * lane) = word[1];
+        put<kNt>(reinterpret_cast<uint32_t*>(code_row + 4 * lane), word[0]);
+        put<kNt>(reinterpret_cast<uint32_t*>(code_row + kHalf + 4 * lane), word[1]);
     } else {
         // e4m3 scale = RNE(fl32(amax / 6)), held at 448; codes = e2m1 RNE of fl32(x / s).
         // fl32(x / s) lands exactly on a rounding midpoint t only when x / s == t (x has 8
@@ -504,8 +520,8 @@ __device__ __forceinline__ void quantize_store_row(uint8_t* __restrict__ pool, u
             }
             half_word[h] = sc == 0 ? 0u : w;  // a zero scale stores all-zero codes
         }
-        *reinterpret_cast<uint16_t*>(code_row + 2 * lane) = static_cast<uint16_t>(half_word[0]);
-        *reinterpret_cast<uint16_t*>(code_row + kHalf / 2 + 2 * lane) = static_cast<uint16_t>(half_word[1]);
+        put<kNt>(reinterpret_cast<uint16_t*>(code_row + 2 * lane), static_cast<uint16_t>(half_word[0]));
+        put<kNt>(reinterpret_cast<uint16_t*>(code_row + kHalf / 2 + 2 * lane), static_cast<uint16_t>(half_word[1]));
     }
 
     // Scale row: lanes 0 and 32 hold the dwords of blocks 0-3 / 4-7 (first half) and
@@ -514,10 +530,10 @@ __device__ __forceinline__ void quantize_store_row(uint8_t* __restrict__ pool, u
     const uint32_t w1 = gather_block_bytes(sbyte[1], lane);
     if ((lane & 31) == 0) {
         const int q = lane >> 5;
-        *reinterpret_cast<uint32_t*>(scale_row + 4 * q) = w0;
-        *reinterpret_cast<uint32_t*>(scale_row + 8 + 4 * q) = w1;
+        put<kNt>(reinterpret_cast<uint32_t*>(scale_row + 4 * q), w0);
+        put<kNt>(reinterpret_cast<uint32_t*>(scale_row + 8 + 4 * q), w1);
         if constexpr (L == Layout::V41_FP4)
-            *reinterpret_cast<uint2*>(scale_row + kBlocks + 8 * q) = make_uint2(0u, 0u);
+            put<kNt>(reinterpret_cast<uint64_t*>(scale_row + kBlocks + 8 * q), uint64_t{0});
     }
 }
 

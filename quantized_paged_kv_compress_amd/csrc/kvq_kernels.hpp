@@ -57,7 +57,8 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void store_kernel(
 // positions, slots and cos/sin rows are shared by all layers (after the first layer they
 // come from L2).  Measured on MI355X at 61 layers x 512 tokens, cold: within about 20 %
 // of a memory twin that makes the same loads and stores with no arithmetic; giving a
-// wavefront 2 or 4 layers of one token is no faster.
+// wavefront 2 or 4 layers of one token is no faster; non-temporal row stores are 6 %
+// faster than plain ones.
 constexpr int kMaxLayers = 64;
 
 struct LayerPtrs {
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void store_layers_kernel(
     rope_load_cs(cos_sin + static_cast<int64_t>(valid ? p : 0) * kRopeDim, lane, cs);
     if (!valid) return;
     rope_apply(v, cs, lane);
-    quantize_store_row<L>(layers.pool[layer], static_cast<uint32_t>(slot), v, lane);
+    quantize_store_row<L, true>(layers.pool[layer], static_cast<uint32_t>(slot), v, lane);
 }
 
 // ------------------------------------------------------------------ ratio 1 (c1)
@@ -215,7 +216,8 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_short_kernel(
 // the window's first score row as the reference; ratios up to 4 are a single chunk (all
 // loads issued at once).  The loads and the cos/sin gather are issued before the slot /
 // position checks, which only gate the store; rows past R (last block) read row R-1 and
-// store nothing.
+// store nothing.  From ratio 16 on the row is written with non-temporal stores (measured
+// 2-4 % faster at 16 and 32; at ratio 8 plain stores are faster).
 template <int kChunk>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ kv, const float* __restrict__ score,
                                            int64_t base, int64_t ld, int lane, float (&x)[kChunk][8],
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_wave_kernel(
     for (int e = 0; e < 8; ++e) v[e] = pool_result(st.l[e], st.acc[e]);
     rope_apply(v, cs, lane);
     if (!valid) return;
-    quantize_store_row<L>(pool, static_cast<uint32_t>(slot), v, lane);
+    quantize_store_row<L, (kRatio >= 16)>(pool, static_cast<uint32_t>(slot), v, lane);
 }
 
 // ------------------------------------------------------------------ long-window compressor
@@ -284,6 +286,7 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_wave_kernel(
 // rotates, quantises and stores the row.  Measured on MI355X: ratio 128 is fastest with 4
 // wavefronts, 1-row chunks and 2 chunks in flight, ratio 64 with 2 wavefronts, 2-row
 // chunks and 2 in flight; 8 wavefronts per row run 10-20 % slower with float64 pooling.
+// The row is written with non-temporal stores: 3-4 % faster than plain ones at both ratios.
 // This lane's 8 channels (two-half mapping) of a channel-indexed row held in LDS.
 __device__ __forceinline__ void load_lds_f32x8(const float* row, int lane, float (&v)[8]) {
 #pragma unroll
@@ -409,7 +412,7 @@ __global__ __launch_bounds__(kWave * kWaves) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = pool_result(st.l[e], st.acc[e]);
     rope_apply(v, cs, lane);
-    quantize_store_row<L>(pool, static_cast<uint32_t>(slot), v, lane);
+    quantize_store_row<L, true>(pool, static_cast<uint32_t>(slot), v, lane);
 }
 
 // ------------------------------------------------------------------ decode-step compressor state
@@ -524,8 +527,10 @@ __device__ __forceinline__ void load_stored_row(const uint8_t* __restrict__ pg, 
 }
 
 // decode(code) * decode(scale) in fp32, rounded to bf16; NaN codes or scales give 0x7FC0.
-// Writes the lane's 8 bf16 values (16 bytes) at dst.
-template <Layout L>
+// Writes the lane's 8 bf16 values (16 bytes) at dst, plain or non-temporal (kNt).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <Layout L, bool kNt = false>
 __device__ __forceinline__ void dequant_lane(const uint32_t (&cw)[2], uint32_t sb, uint16_t* __restrict__ dst,
                                              int lane) {
     uint32_t o[8];
@@ -552,12 +557,8 @@ __device__ __forceinline__ void dequant_lane(const uint32_t (&cw)[2], uint32_t s
             o[e] = nan_scale ? 0x7FC0u : bf16_rne_bits(val);
         }
     }
-    uint4 st;
-    st.x = o[0] | (o[1] << 16);
-    st.y = o[2] | (o[3] << 16);
-    st.z = o[4] | (o[5] << 16);
-    st.w = o[6] | (o[7] << 16);
-    *reinterpret_cast<uint4*>(dst + kElemsPerLane * lane) = st;
+    const u32x4 st = {o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16)};
+    put<kNt>(reinterpret_cast<u32x4*>(dst + kElemsPerLane * lane), st);
 }
 
 // Whole pages: each wavefront dequantises kRowsPerWave consecutive rows of one listed
@@ -585,7 +586,8 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void dequant_kernel(
 }
 
 // Token gather: output row g is the dequantised row at slots[g]; rows whose slot is
-// outside the pool are left untouched.
+// outside the pool are left untouched.  Non-temporal stores (14 % faster than plain ones
+// for 16,384 rows; the page kernel above gains nothing from them).
 template <Layout L>
 __global__ __launch_bounds__(kWave * kRowsPerBlock) void dequant_slots_kernel(
     const uint8_t* __restrict__ pool, int64_t nslots, const int32_t* __restrict__ slots, int64_t n,
@@ -599,7 +601,7 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void dequant_slots_kernel(
     const uint8_t* pg = pool + static_cast<int64_t>(slot >> kPageBits) * kPB;
     uint32_t cw[2], sb;
     load_stored_row<L>(pg, slot & ((1 << kPageBits) - 1), lane, cw, sb);
-    dequant_lane<L>(cw, sb, out + g * kHeadDim, lane);
+    dequant_lane<L, true>(cw, sb, out + g * kHeadDim, lane);
 }
 
 // ------------------------------------------------------------------ full -> SWA slots
