@@ -245,16 +245,23 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def mixed_graph(kvq, m, cs, reps=20):
-    """The mixed FP4 step (translate -> ratio-4 compress at the translated slots -> dequant
-    of the touched pages) captured as one HIP graph and replayed; each replay is timed by
-    stream events around it, with a 512 MiB write before it so that its inputs are cold."""
+def mixed_graph(kvq, m, cs, fused=True, reps=20):
+    """The mixed FP4 step (full -> SWA translation, ratio-4 compress at the translated slots,
+    dequant of the touched pages) captured as one HIP graph and replayed; each replay is
+    timed by stream events around it, with a 512 MiB write before it so that its inputs
+    are cold.  fused: the translation runs inside the compressor's launch
+    (kv_compress_store_translate, two launches in all); otherwise kv_translate_slots is a
+    launch of its own (three)."""
     import numpy as np
     import torch
 
     def seq():
-        loc = kvq.kv_translate_slots(m["table"], m["full"], m["loc"])
-        kvq.kv_compress_store(m["pool"], kvq.V41_FP4, m["kv"], m["sc"], 4, m["pos"], cs, loc)
+        if fused:
+            kvq.kv_compress_store_translate(m["pool"], kvq.V41_FP4, m["kv"], m["sc"], 4, m["pos"], cs,
+                                            m["table"], m["full"], m["loc"])
+        else:
+            loc = kvq.kv_translate_slots(m["table"], m["full"], m["loc"])
+            kvq.kv_compress_store(m["pool"], kvq.V41_FP4, m["kv"], m["sc"], 4, m["pos"], cs, loc)
         kvq.kv_dequant(m["pool"], kvq.V41_FP4, m["page_ids"], m["ws"])
 
     s = torch.cuda.Stream()
@@ -435,9 +442,9 @@ PROFILE_RUNS = {
 SHORT_NAMES = {
     "compress_long_kernel<(kvq::Layout)1, 128": "compress_long<V41, ratio 128> (C128A)",
     "compress_short_kernel<(kvq::Layout)1, 4>": "compress_short<V41, ratio 4> (C4A)",
-    "compress_short_kernel<(kvq::Layout)2, 4>": "compress_short<V41_FP4, ratio 4> (mixed step)",
+    "compress_short_kernel<(kvq::Layout)2, 4>": "compress_short<V41_FP4, 4> (mixed, translating)",
     "dequant_kernel<(kvq::Layout)2": "dequant<V41_FP4> (mixed step)",
-    "translate_kernel": "translate (mixed step)",
+    "translate_kernel": "translate (three-launch mixed graph)",
     "__amd_rocclr_copyBuffer": "__amd_rocclr_copyBuffer (1 GiB device copy)",
 }
 COPY_KEY = SHORT_NAMES["__amd_rocclr_copyBuffer"]
@@ -754,7 +761,9 @@ def main():
         f"{time.perf_counter() - t_gen:.1f} s")
 
     c4, c128 = inputs["c4a"], inputs["c128a"]
-    names = ["translate", "compress_mixed_fp4", "dequant_fp4", "compress_c4a", "compress_c128a"]
+    # the mixed step's compressor translates its full-pool slots itself
+    # (kv_compress_store_translate) and leaves them in m["loc"] for later consumers
+    names = ["compress_mixed_fp4", "dequant_fp4", "compress_c4a", "compress_c128a"]
 
     # Kernel durations come from events that a kernel's own dispatch records
     # (kvq_profile_next_launch); each armed launch adds a few microseconds of gap on the
@@ -762,7 +771,7 @@ def main():
     # kernels' durations come from one more pass of the same steps right after it.  Every
     # kernel of a timed step is also bracketed by events recorded on the stream (these hold
     # the gap between commands as well).
-    timed_armed = {3, 4}
+    timed_armed = {2, 3}
 
     def step(k=None, armed=(), clocks=None, ev=None):
         def arm(j):
@@ -770,25 +779,23 @@ def main():
                 clocks[k].arm(j)
         if ev: ev[0].record()
         arm(0)
-        loc = kvq.kv_translate_slots(m["table"], m["full"], m["loc"])
+        kvq.kv_compress_store_translate(m["pool"], kvq.V41_FP4, m["kv"], m["sc"], 4, m["pos"], cs,
+                                        m["table"], m["full"], m["loc"])
         if ev: ev[1].record()
         arm(1)
-        kvq.kv_compress_store(m["pool"], kvq.V41_FP4, m["kv"], m["sc"], 4, m["pos"], cs, loc)
+        kvq.kv_dequant(m["pool"], kvq.V41_FP4, m["page_ids"], m["ws"])
         if ev: ev[2].record()
         arm(2)
-        kvq.kv_dequant(m["pool"], kvq.V41_FP4, m["page_ids"], m["ws"])
+        kvq.kv_compress_store(c4["pool"], kvq.V41, c4["kv"], c4["sc"], 4, c4["pos"], cs, c4["slots"])
         if ev: ev[3].record()
         arm(3)
-        kvq.kv_compress_store(c4["pool"], kvq.V41, c4["kv"], c4["sc"], 4, c4["pos"], cs, c4["slots"])
-        if ev: ev[4].record()
-        arm(4)
         kvq.kv_compress_store(c128["pool"], kvq.V41, c128["kv"], c128["sc"], 128, c128["pos"], cs,
                               c128["slots"])
-        if ev: ev[5].record()
+        if ev: ev[4].record()
 
     for _ in range(args.warmup):
         step()
-    stream_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    stream_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     clocks = [DispatchTimer(kvq, len(names)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -836,8 +843,8 @@ def main():
 
     pb_fp4, pb_v41 = kvq.page_bytes(kvq.V41_FP4), kvq.page_bytes(kvq.V41)
     alg = {
-        "translate": bytes_translate(m["R"], mx["cap"]),
-        "compress_mixed_fp4": bytes_compress(m["R"], 4, kvq.bytes_per_token(kvq.V41_FP4)),
+        "compress_mixed_fp4": (bytes_compress(m["R"], 4, kvq.bytes_per_token(kvq.V41_FP4))
+                               + bytes_translate(m["R"], mx["cap"])),
         "dequant_fp4": bytes_dequant(mx["page_ids"].size, pb_fp4),
         "compress_c4a": bytes_compress(16384, 4, kvq.bytes_per_token(kvq.V41)),
         "compress_c128a": bytes_compress(16384, 128, kvq.bytes_per_token(kvq.V41)),
@@ -856,13 +863,18 @@ def main():
             kernels[n]["rows/s"] = round(rows[n] / (avg_ms[n] * 1e-3), 1)
     rows_per_step = sum(rows.values())
     dom = "compress_c128a"
-    mixed_alg = alg["translate"] + alg["compress_mixed_fp4"] + alg["dequant_fp4"]
-    g_us, g_p10, g_p90 = mixed_graph(kvq, m, cs)
+    mixed_alg = alg["compress_mixed_fp4"] + alg["dequant_fp4"]
+    g_us, g_p10, g_p90 = mixed_graph(kvq, m, cs, fused=True)
+    s_us, _, _ = mixed_graph(kvq, m, cs, fused=False)
     mixed_graph_line = {"us": round(g_us, 2), "us_p10": round(g_p10, 2), "us_p90": round(g_p90, 2),
                   "alg_bytes": mixed_alg, "GB/s": round(mixed_alg / (g_us * 1e-6) / 1e9, 1),
                   "frac_of_peak": round(mixed_alg / (g_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                  "method": "translate + compress + dequant replayed as one HIP graph, cold inputs, "
-                            "median of 20 replays timed by stream events around each"}
+                  "separate_translate_us": round(s_us, 2),
+                  "separate_translate_frac_of_peak": round(mixed_alg / (s_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                  "method": "compress with the translation fused in (kv_compress_store_translate) + dequant "
+                            "replayed as one HIP graph, cold inputs, median of 20 replays timed by stream "
+                            "events around each; separate_translate: the same step with kv_translate_slots "
+                            "as a launch of its own"}
     log(f"mixed step as one graph: {mixed_graph_line['us']} us, {mixed_graph_line['frac_of_peak']} of peak")
     traffic = read_traffic(alg[dom])
 
@@ -920,7 +932,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": ("mixed V41_FP4 step (translate + ratio-4 compress + dequant) + C4A "
+            "workload": ("mixed V41_FP4 step (ratio-4 compress with the full->SWA slot translation "
+                         "fused in + dequant) + C4A "
                          "(R=16384, ratio 4, V41) + C128A (R=16384, ratio 128, V41); fp32 kv/score "
                          "x 512 channels, 64-token pages"),
             "rows_per_step": rows_per_step,

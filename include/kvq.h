@@ -74,7 +74,8 @@ extern "C" {
                               num_pages > 2^32                                     */
 #define KVQ_ELAYOUT (-2)   /* layout id is not KVQ_LAYOUT_V41 / KVQ_LAYOUT_V41_FP4 */
 #define KVQ_ERATIO (-3)    /* ratio not built (supported: 1, 2, 4, 8, 16, 32, 64, 128) */
-#define KVQ_ECAPACITY (-4) /* kv_translate_slots with n > cap; nothing enqueued   */
+#define KVQ_ECAPACITY (-4) /* more slots than the translation buffer holds (n > cap
+                              or R > cap); nothing enqueued                        */
 #define KVQ_ELAUNCH (-5)   /* the HIP runtime rejected the kernel launch          */
 
 /* ---- size limits of one call (larger requests return KVQ_EINVAL) --------------- */
@@ -188,6 +189,28 @@ int kv_compress_store(int32_t layout, void* pool, int64_t num_pages, const float
                       const float* score, int64_t ld, int32_t ratio, const int32_t* pos,
                       const float* cos_sin, int64_t max_pos, const int32_t* slots,
                       int64_t R, void* stream);
+
+/* kv_compress_store_translate -- kv_compress_store with the step's full -> SWA slot
+ * translation fused in ([P2] section 1: the translation is computed once per step; here
+ * the first compressor of the step computes it and leaves it in out_loc for the later
+ * consumers).  The result is that of
+ *   kv_translate_slots(table, table_len, full_loc, R, out_loc, cap, stream);
+ *   kv_compress_store(..., slots = out_loc, R, stream);
+ * (out_loc[i] = table[full_loc[i]] for i < R, -1 for a full slot outside [0, table_len),
+ * out_loc[R:cap] = 0; row i is stored at out_loc[i]), in one launch: each row looks its
+ * slot up in the table itself.  When the zero tail is long against the grid (more than
+ * 16 chunks of 64 entries per wavefront) the translation runs as its own launch first.
+ * Errors: those of kv_compress_store; cap < 0, cap > 2^31 - 1 or table_len < 0 give
+ * KVQ_EINVAL; R > cap gives KVQ_ECAPACITY and enqueues nothing.  R == 0 only zeroes
+ * out_loc[0:cap].  out_loc must not overlap table or full_loc.
+ *   table      device int32[table_len]
+ *   full_loc   device int32[R]: full-pool slots of the output rows
+ *   out_loc    device int32[cap]: the translated slots */
+int kv_compress_store_translate(int32_t layout, void* pool, int64_t num_pages, const float* kv,
+                                const float* score, int64_t ld, int32_t ratio, const int32_t* pos,
+                                const float* cos_sin, int64_t max_pos, const int32_t* table,
+                                int64_t table_len, const int32_t* full_loc, int32_t* out_loc,
+                                int64_t cap, int64_t R, void* stream);
 
 /* Bytes of one sequence's decode-step compressor state (kv_compress_state_update). */
 int64_t kvq_compress_state_bytes(void);  /* 10240 */

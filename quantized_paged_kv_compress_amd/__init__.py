@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "V41", "V41_FP4", "KVQError", "load_library", "profile_next_launch", "bytes_per_token", "page_bytes",
     "code_row_bytes", "scale_row_bytes", "new_pool", "kv_store", "kv_store_rope", "kv_store_rope_layers", "kv_store_norm_rope",
-    "kv_compress_store", "kv_compress_state_update", "new_compress_state", "compress_state_bytes", "kv_dequant", "kv_dequant_slots", "kv_translate_slots", "SUPPORTED_RATIOS",
+    "kv_compress_store", "kv_compress_store_translate", "kv_compress_state_update", "new_compress_state", "compress_state_bytes", "kv_dequant", "kv_dequant_slots", "kv_translate_slots", "SUPPORTED_RATIOS",
 ]
 
 V41 = 1
@@ -71,6 +71,8 @@ def load_library() -> ctypes.CDLL:
         "kv_store_norm_rope": [i32, vp, i64, vp, i64, vp, ctypes.c_float, vp, vp, i64, vp, i64, vp],
         "kv_store_rope_layers": [i32, vp, i64, vp, i64, i32, vp, vp, i64, vp, i64, vp],
         "kv_compress_store": [i32, vp, i64, vp, vp, i64, i32, vp, vp, i64, vp, i64, vp],
+        "kv_compress_store_translate": [i32, vp, i64, vp, vp, i64, i32, vp, vp, i64, vp, i64, vp, vp, i64,
+                                        i64, vp],
         "kv_compress_state_update": [i32, vp, i64, vp, vp, i64, i32, vp, vp, vp, i64, vp, vp, i64, vp,
                                      i64, vp],
         "kv_dequant": [i32, vp, i64, vp, i64, vp, vp],
@@ -272,6 +274,37 @@ def kv_compress_store(pool, layout, kv, score, ratio, pos, cos_sin, slots, strea
     _raise("kv_compress_store", load_library().kv_compress_store(
         layout, _ptr(pool), num_pages, _ptr(kv), _ptr(score), ld, ratio, _ptr(pos),
         _ptr(cos_sin), cos_sin.shape[0], _ptr(slots), R, _stream(stream)))
+
+
+def kv_compress_store_translate(pool, layout, kv, score, ratio, pos, cos_sin, table, full_loc, out,
+                                stream=None):
+    """kv_translate_slots(table, full_loc, out) and kv_compress_store(..., slots=out[:R]) in
+    one launch: row i is stored at table[full_loc[i]], which is also left in out[i]
+    (out[R:] zeroed).  Returns out[:R], or None when full_loc is longer than out (nothing
+    is written)."""
+    num_pages = _pool(pool, layout)
+    ld = _rows(_dev(kv, "kv", _F32), "kv")
+    if score is not None:
+        if _rows(_dev(score, "score", _F32), "score") != ld or score.shape[0] != kv.shape[0]:
+            raise ValueError("score must match kv in shape and stride")
+    _vec(pos, "pos")
+    _vec(table, "table")
+    _vec(full_loc, "full_loc")
+    _vec(out, "out")
+    _dev(cos_sin, "cos_sin", _F32)
+    if not cos_sin.is_contiguous() or cos_sin.dim() != 2 or cos_sin.shape[1] != ROPE_DIM:
+        raise ValueError("cos_sin: need a contiguous fp32 [max_pos, 64] tensor")
+    R = full_loc.numel()
+    if pos.numel() != R or kv.shape[0] < R * ratio:
+        raise ValueError("kv / pos / full_loc sizes disagree")
+    st = load_library().kv_compress_store_translate(
+        layout, _ptr(pool), num_pages, _ptr(kv), _ptr(score), ld, ratio, _ptr(pos), _ptr(cos_sin),
+        cos_sin.shape[0], _ptr(table), table.numel(), _ptr(full_loc), _ptr(out), out.numel(), R,
+        _stream(stream))
+    if st == KVQ_ECAPACITY:
+        return None
+    _raise("kv_compress_store_translate", st)
+    return out[:R]
 
 
 def compress_state_bytes() -> int:

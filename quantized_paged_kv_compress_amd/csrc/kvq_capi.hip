@@ -84,43 +84,47 @@ int store_impl(int mode, void* pool, int64_t num_pages, const uint16_t* k, int64
 
 template <Layout L>
 int compress_c1(void* pool, int64_t num_pages, const float* kv, int64_t ld, const int32_t* pos,
-                const float* cos_sin, int64_t max_pos, const int32_t* slots, int64_t R, void* stream) {
+                const float* cos_sin, int64_t max_pos, kvq::SlotSrc slots, int64_t R, void* stream) {
     return launch(kvq::compress_c1_kernel<L>, dim3(blocks_for(R, kvq::kRowsPerBlock)),
                   dim3(kvq::kWave * kvq::kRowsPerBlock), stream, static_cast<uint8_t*>(pool),
-                  num_pages << kvq::kPageBits, kv, ld, pos, cos_sin, max_pos, slots, R);
+                  num_pages << kvq::kPageBits, kv, ld, pos, cos_sin, max_pos, slots.slots, slots.table,
+                  slots.table_len, slots.out, slots.cap, R);
 }
 
 template <Layout L, int kRatio>
 int compress_short(void* pool, int64_t num_pages, const float* kv, const float* score, int64_t ld,
                    const int32_t* pos, const float* cos_sin, int64_t max_pos,
-                   const int32_t* slots, int64_t R, void* stream) {
+                   kvq::SlotSrc slots, int64_t R, void* stream) {
     return launch(kvq::compress_short_kernel<L, kRatio>, dim3(blocks_for(R, kvq::kRowsPerBlock)),
                   dim3(kvq::kWave * kvq::kRowsPerBlock), stream, static_cast<uint8_t*>(pool),
-                  num_pages << kvq::kPageBits, kv, score, ld, pos, cos_sin, max_pos, slots, R);
+                  num_pages << kvq::kPageBits, kv, score, ld, pos, cos_sin, max_pos, slots.slots, slots.table,
+                  slots.table_len, slots.out, slots.cap, R);
 }
 
 template <Layout L, int kRatio, int kChunk, int kDepth>
 int compress_wave(void* pool, int64_t num_pages, const float* kv, const float* score, int64_t ld,
                   const int32_t* pos, const float* cos_sin, int64_t max_pos,
-                  const int32_t* slots, int64_t R, void* stream) {
+                  kvq::SlotSrc slots, int64_t R, void* stream) {
     return launch(kvq::compress_wave_kernel<L, kRatio, kChunk, kDepth>, dim3(blocks_for(R, kvq::kRowsPerBlock)),
                   dim3(kvq::kWave * kvq::kRowsPerBlock), stream, static_cast<uint8_t*>(pool),
-                  num_pages << kvq::kPageBits, kv, score, ld, pos, cos_sin, max_pos, slots, R);
+                  num_pages << kvq::kPageBits, kv, score, ld, pos, cos_sin, max_pos, slots.slots, slots.table,
+                  slots.table_len, slots.out, slots.cap, R);
 }
 
 template <Layout L, int kRatio, int kWaves, int kChunk, int kDepth>
 int compress_long(void* pool, int64_t num_pages, const float* kv, const float* score, int64_t ld,
                   const int32_t* pos, const float* cos_sin, int64_t max_pos,
-                  const int32_t* slots, int64_t R, void* stream) {
+                  kvq::SlotSrc slots, int64_t R, void* stream) {
     return launch(kvq::compress_long_kernel<L, kRatio, kWaves, kChunk, kDepth>, dim3(static_cast<unsigned>(R)),
                   dim3(kvq::kWave * kWaves), stream, static_cast<uint8_t*>(pool),
-                  num_pages << kvq::kPageBits, kv, score, ld, pos, cos_sin, max_pos, slots, R);
+                  num_pages << kvq::kPageBits, kv, score, ld, pos, cos_sin, max_pos, slots.slots, slots.table,
+                  slots.table_len, slots.out, slots.cap, R);
 }
 
 template <Layout L>
 int compress_dispatch(int32_t ratio, void* pool, int64_t num_pages, const float* kv,
                       const float* score, int64_t ld, const int32_t* pos, const float* cos_sin,
-                      int64_t max_pos, const int32_t* slots, int64_t R, void* stream) {
+                      int64_t max_pos, kvq::SlotSrc slots, int64_t R, void* stream) {
     // per ratio: wave <rows per chunk, chunks in flight + 1>, long <wavefronts, rows per
     // chunk, chunks in flight + 1>; measured fastest on MI355X
     const auto* sc = score;
@@ -260,10 +264,11 @@ int kv_store_norm_rope(int32_t layout, void* pool, int64_t num_pages, const uint
                         stream);
 }
 
-int kv_compress_store(int32_t layout, void* pool, int64_t num_pages, const float* kv,
-                      const float* score, int64_t ld, int32_t ratio, const int32_t* pos,
-                      const float* cos_sin, int64_t max_pos, const int32_t* slots, int64_t R,
-                      void* stream) {
+// Checks of a compressor call apart from its slots (layout, ratio, sizes, the input
+// pointers when there is work, strides, alignment).
+static int compress_check(int32_t layout, const void* pool, int64_t num_pages, const float* kv,
+                          const float* score, int64_t ld, int32_t ratio, const int32_t* pos,
+                          const float* cos_sin, int64_t max_pos, int64_t R) {
     if (!known_layout(layout)) return KVQ_ELAYOUT;
     if (ratio != 1 && ratio != 2 && ratio != 4 && ratio != 8 && ratio != 16 && ratio != 32 &&
         ratio != 64 && ratio != 128)
@@ -272,13 +277,55 @@ int kv_compress_store(int32_t layout, void* pool, int64_t num_pages, const float
         max_pos <= 0)
         return KVQ_EINVAL;
     if (R == 0) return KVQ_OK;
-    if (!pool || !kv || (ratio > 1 && !score) || !pos || !cos_sin || !slots) return KVQ_EINVAL;
+    if (!pool || !kv || (ratio > 1 && !score) || !pos || !cos_sin) return KVQ_EINVAL;
     if (ld < kvq::kHeadDim || ld % 4 != 0) return KVQ_EINVAL;
     if (!aligned16(pool) || !aligned16(kv) || (ratio > 1 && !aligned16(score)) || !aligned16(cos_sin))
         return KVQ_EINVAL;
+    return KVQ_OK;
+}
+
+static int compress_launch(int32_t layout, void* pool, int64_t num_pages, const float* kv, const float* score,
+                           int64_t ld, int32_t ratio, const int32_t* pos, const float* cos_sin,
+                           int64_t max_pos, kvq::SlotSrc src, int64_t R, void* stream) {
     if (layout == KVQ_LAYOUT_V41)
-        return compress_dispatch<Layout::V41>(ratio, pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
-    return compress_dispatch<Layout::V41_FP4>(ratio, pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, slots, R, stream);
+        return compress_dispatch<Layout::V41>(ratio, pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, src, R, stream);
+    return compress_dispatch<Layout::V41_FP4>(ratio, pool, num_pages, kv, score, ld, pos, cos_sin, max_pos, src, R, stream);
+}
+
+int kv_compress_store(int32_t layout, void* pool, int64_t num_pages, const float* kv,
+                      const float* score, int64_t ld, int32_t ratio, const int32_t* pos,
+                      const float* cos_sin, int64_t max_pos, const int32_t* slots, int64_t R,
+                      void* stream) {
+    const int st = compress_check(layout, pool, num_pages, kv, score, ld, ratio, pos, cos_sin, max_pos, R);
+    if (st != KVQ_OK || R == 0) return st;
+    if (!slots) return KVQ_EINVAL;
+    return compress_launch(layout, pool, num_pages, kv, score, ld, ratio, pos, cos_sin, max_pos,
+                           kvq::SlotSrc{slots, nullptr, 0, nullptr, R, R}, R, stream);
+}
+
+int kv_compress_store_translate(int32_t layout, void* pool, int64_t num_pages, const float* kv,
+                                const float* score, int64_t ld, int32_t ratio, const int32_t* pos,
+                                const float* cos_sin, int64_t max_pos, const int32_t* table,
+                                int64_t table_len, const int32_t* full_loc, int32_t* out_loc, int64_t cap,
+                                int64_t R, void* stream) {
+    const int st = compress_check(layout, pool, num_pages, kv, score, ld, ratio, pos, cos_sin, max_pos, R);
+    if (st != KVQ_OK) return st;
+    if (cap < 0 || cap > kMaxCap || table_len < 0) return KVQ_EINVAL;
+    if (R > cap) return KVQ_ECAPACITY;
+    if (R == 0) return kv_translate_slots(table, table_len, full_loc, 0, out_loc, cap, stream);
+    if (!table || !full_loc || !out_loc) return KVQ_EINVAL;
+    // The grid's wavefronts zero out[R:cap] between them; a tail longer than
+    // kMaxTailChunks chunks of 64 per wavefront is left to the translation kernel instead.
+    const int64_t waves = ratio == 128 ? R * 4 : ratio == 64 ? R * 2
+                                                             : int64_t(blocks_for(R, kvq::kRowsPerBlock)) * kvq::kRowsPerBlock;
+    if ((cap - R + 63) / 64 > kvq::kMaxTailChunks * waves) {
+        const int t = kv_translate_slots(table, table_len, full_loc, R, out_loc, cap, stream);
+        if (t != KVQ_OK) return t;
+        return compress_launch(layout, pool, num_pages, kv, score, ld, ratio, pos, cos_sin, max_pos,
+                               kvq::SlotSrc{out_loc, nullptr, 0, nullptr, R, R}, R, stream);
+    }
+    return compress_launch(layout, pool, num_pages, kv, score, ld, ratio, pos, cos_sin, max_pos,
+                           kvq::SlotSrc{full_loc, table, table_len, out_loc, R, cap}, R, stream);
 }
 
 int kv_compress_state_update(int32_t layout, void* pool, int64_t num_pages, void* state, int32_t* count,

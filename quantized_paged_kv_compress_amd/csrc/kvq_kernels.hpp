@@ -87,6 +87,48 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void store_layers_kernel(
     quantize_store_row<L, true>(layers.pool[layer], static_cast<uint32_t>(slot), v, lane);
 }
 
+// ------------------------------------------------------------------ where a compressed row's slot comes from
+// Either the caller's slots[i], or -- the full -> SWA translation of the SGLang SWA-hoisting
+// page, section 1, fused into the compressor -- table[full[i]] (-1 for a full slot outside
+// the table), which is also written to out[i] for the later consumers of the step; the
+// wavefronts of the grid then zero out[n:cap] between them, as the separate translation
+// does.  table == nullptr selects the plain form.  The kernels take the pointers as
+// separate __restrict__ parameters (and rebuild this struct): only then can the compiler
+// read slots and table through the scalar cache, off the vector-memory counter that the
+// window loads are waited on.
+struct SlotSrc {
+    const int32_t* slots;  // slots, or full-pool slots when table is set
+    const int32_t* table;
+    int64_t table_len;
+    int32_t* out;          // translated slots [cap]
+    int64_t n, cap;
+};
+
+__device__ __forceinline__ int32_t row_slot(const SlotSrc& src, int64_t i) {
+    const int32_t s = src.slots[i];
+    if (src.table == nullptr) return s;
+    return (s >= 0 && s < src.table_len) ? src.table[s] : -1;
+}
+
+// Row i's translated slot, written back by one lane (fused form only).
+__device__ __forceinline__ void put_translated(const SlotSrc& src, int64_t i, int32_t slot, int lane) {
+    if (src.table != nullptr && lane == 0 && i < src.n) src.out[i] = slot;
+}
+
+// Wavefront `wave` of `num_waves` zeroes its share of out[n:cap] in 64-entry chunks
+// (fused form only; the host takes the fused form only when every wavefront has at most
+// kMaxTailChunks chunks).
+constexpr int64_t kMaxTailChunks = 16;
+
+__device__ __forceinline__ void clear_tail(const SlotSrc& src, int64_t wave, int64_t num_waves, int lane) {
+    if (src.table == nullptr) return;
+    const int64_t chunks = (src.cap - src.n + 63) / 64;
+    for (int64_t c = wave; c < chunks; c += num_waves) {
+        const int64_t j = src.n + c * 64 + lane;
+        if (j < src.cap) src.out[j] = 0;
+    }
+}
+
 // ------------------------------------------------------------------ ratio 1 (c1)
 // A one-row window pools to the row itself: round the fp32 kv row to bf16, RoPE, quantise,
 // store (scores are not read).  One wavefront per row, 4 rows per workgroup; rows past R
@@ -95,17 +137,24 @@ template <Layout L>
 __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_c1_kernel(
     uint8_t* __restrict__ pool, int64_t nslots, const float* __restrict__ kv, int64_t ld,
     const int32_t* __restrict__ pos, const float* __restrict__ cos_sin, int64_t max_pos,
-    const int32_t* __restrict__ slots, int64_t R) {
+    const int32_t* __restrict__ slots, const int32_t* __restrict__ table,
+    int64_t table_len, int32_t* __restrict__ out, int64_t cap, int64_t R) {
+    const SlotSrc src{slots, table, table_len, out, R, cap};
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t i_raw = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave_id();
     const int64_t i = i_raw < R ? i_raw : R - 1;
     float v[8];
     load_row_f32(kv + i * ld, lane, v);
-    const int32_t slot = slots[i];
+    // the cos/sin gather depends on the position only, so that it is not held up behind
+    // the slot (and, when translating, the table lookup); the slot only gates the store
     const int32_t p = pos[i];
-    const bool valid = i_raw < R && slot >= 0 && slot < nslots && p >= 0 && p < max_pos;
+    const bool pos_ok = p >= 0 && p < max_pos;
     RopeCS cs;
-    rope_load_cs(cos_sin + static_cast<int64_t>(valid ? p : 0) * kRopeDim, lane, cs);
+    rope_load_cs(cos_sin + static_cast<int64_t>(pos_ok ? p : 0) * kRopeDim, lane, cs);
+    clear_tail(src, i_raw, static_cast<int64_t>(gridDim.x) * kRowsPerBlock, lane);
+    const int32_t slot = row_slot(src, i);
+    put_translated(src, i_raw, slot, lane);
+    const bool valid = i_raw < R && pos_ok && slot >= 0 && slot < nslots;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = round_bf16(v[e]);
     rope_apply(v, cs, lane);
@@ -137,8 +186,10 @@ template <Layout L, int kRatio>
 __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_short_kernel(
     uint8_t* __restrict__ pool, int64_t nslots, const float* __restrict__ kv,
     const float* __restrict__ score, int64_t ld, const int32_t* __restrict__ pos,
-    const float* __restrict__ cos_sin, int64_t max_pos, const int32_t* __restrict__ slots,
+    const float* __restrict__ cos_sin, int64_t max_pos, const int32_t* __restrict__ slots, const int32_t* __restrict__ table,
+    int64_t table_len, int32_t* __restrict__ out, int64_t cap,
     int64_t R) {
+    const SlotSrc src{slots, table, table_len, out, R, cap};
     static_assert(kRatio == 2 || kRatio == 4, "short window");
     constexpr float kU = 0x1p-24f;
     const int lane = threadIdx.x & (kWave - 1);
@@ -152,11 +203,16 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_short_kernel(
         load_row_f32(kv + base + j * ld, lane, x[j]);
         load_row_f32(score + base + j * ld, lane, s[j]);
     }
-    const int32_t slot = slots[i];
+    // the cos/sin gather depends on the position only, so that it is not held up behind
+    // the slot (and, when translating, the table lookup); the slot only gates the store
     const int32_t p = pos[i];
-    const bool valid = i_raw < R && slot >= 0 && slot < nslots && p >= 0 && p < max_pos;
+    const bool pos_ok = p >= 0 && p < max_pos;
     RopeCS cs;
-    rope_load_cs(cos_sin + static_cast<int64_t>(valid ? p : 0) * kRopeDim, lane, cs);
+    rope_load_cs(cos_sin + static_cast<int64_t>(pos_ok ? p : 0) * kRopeDim, lane, cs);
+    clear_tail(src, i_raw, static_cast<int64_t>(gridDim.x) * kRowsPerBlock, lane);
+    const int32_t slot = row_slot(src, i);
+    put_translated(src, i_raw, slot, lane);
+    const bool valid = i_raw < R && pos_ok && slot >= 0 && slot < nslots;
 
     float v[8], mx[8];
     uint32_t redo = 0;  // bit e: channel e is recomputed in float64
@@ -233,8 +289,10 @@ template <Layout L, int kRatio, int kChunk, int kDepth>
 __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_wave_kernel(
     uint8_t* __restrict__ pool, int64_t nslots, const float* __restrict__ kv,
     const float* __restrict__ score, int64_t ld, const int32_t* __restrict__ pos,
-    const float* __restrict__ cos_sin, int64_t max_pos, const int32_t* __restrict__ slots,
+    const float* __restrict__ cos_sin, int64_t max_pos, const int32_t* __restrict__ slots, const int32_t* __restrict__ table,
+    int64_t table_len, int32_t* __restrict__ out, int64_t cap,
     int64_t R) {
+    const SlotSrc src{slots, table, table_len, out, R, cap};
     constexpr int kChunks = kRatio / kChunk;
     static_assert(kRatio % kChunk == 0 && kDepth >= 2, "window split");
     __shared__ double tab[256];
@@ -249,13 +307,19 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_wave_kernel(
 #pragma unroll
     for (int c = 0; c < kDepth - 1 && c < kChunks; ++c)
         load_chunk<kChunk>(kv, score, base + c * step, ld, lane, x[c], sc[c]);
-    const int32_t slot = slots[i];
+    // the cos/sin gather depends on the position only, so that it is not held up behind
+    // the slot (and, when translating, the table lookup); the slot only gates the store
     const int32_t p = pos[i];
-    const bool valid = i_raw < R && slot >= 0 && slot < nslots && p >= 0 && p < max_pos;
+    const bool pos_ok = p >= 0 && p < max_pos;
     RopeCS cs;
-    rope_load_cs(cos_sin + static_cast<int64_t>(valid ? p : 0) * kRopeDim, lane, cs);
+    rope_load_cs(cos_sin + static_cast<int64_t>(pos_ok ? p : 0) * kRopeDim, lane, cs);
     tcopy.put(tab);
     __syncthreads();  // the exp table is in LDS
+    // after the barrier, whose wait would otherwise include the slot's (table) lookup
+    clear_tail(src, i_raw, static_cast<int64_t>(gridDim.x) * kRowsPerBlock, lane);
+    const int32_t slot = row_slot(src, i);
+    put_translated(src, i_raw, slot, lane);
+    const bool valid = i_raw < R && pos_ok && slot >= 0 && slot < nslots;
 
     PoolF64 st;
     pool_init(st, sc[0][0]);
@@ -311,8 +375,10 @@ template <Layout L, int kRatio, int kWaves, int kChunk, int kDepth>
 __global__ __launch_bounds__(kWave * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void compress_long_kernel(
     uint8_t* __restrict__ pool, int64_t nslots, const float* __restrict__ kv,
     const float* __restrict__ score, int64_t ld, const int32_t* __restrict__ pos,
-    const float* __restrict__ cos_sin, int64_t max_pos, const int32_t* __restrict__ slots,
+    const float* __restrict__ cos_sin, int64_t max_pos, const int32_t* __restrict__ slots, const int32_t* __restrict__ table,
+    int64_t table_len, int32_t* __restrict__ out, int64_t cap,
     int64_t R) {
+    const SlotSrc src{slots, table, table_len, out, R, cap};
     constexpr int kChunks = kRatio / (kWaves * kChunk);   // chunks per wavefront
     static_assert(kRatio % (kWaves * kChunk) == 0 && kChunks >= 1 && kDepth >= 2, "window split");
     // partial states of wavefronts 1..kWaves-1, channel-indexed; the exp table
@@ -322,7 +388,9 @@ __global__ __launch_bounds__(kWave * kWaves) __attribute__((amdgpu_waves_per_eu(
     __shared__ double tab[256];
 
     const int64_t i = blockIdx.x;
-    const int32_t slot = slots[i];
+    clear_tail(src, i * kWaves + wave_id(), static_cast<int64_t>(gridDim.x) * kWaves, threadIdx.x & (kWave - 1));
+    const int32_t slot = row_slot(src, i);
+    if (threadIdx.x == 0) put_translated(src, i, slot, 0);
     const int32_t p = pos[i];
     if (slot < 0 || slot >= nslots || p < 0 || p >= max_pos) return;  // whole workgroup
     ExpTableCopy<kWave * kWaves> tcopy;

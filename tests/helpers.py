@@ -65,6 +65,8 @@ def code_ords(codes, layout):
 def compare_compressed(got_pool, ref_pool, layout, slots, min_equal=0.999, label=""):
     """Apply the compressor comparison rule on the rows at `slots`; returns the fraction of
     identical codes and prints how many codes differ."""
+    if len(slots) == 0:
+        return 1.0
     gc, gs = rows_of(got_pool, layout, slots)
     rc, rs = rows_of(ref_pool, layout, slots)
     if layout == FP4:

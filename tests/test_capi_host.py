@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     for want in ("kv_store", "kv_store_rope", "kv_store_norm_rope", "kv_compress_store",
                  "kv_compress_state_update", "kv_dequant_slots", "kv_dequant",
                  "kv_translate_slots", "kvq_bytes_per_token", "kvq_page_bytes", "kv_store_rope_layers",
-                 "kvq_profile_next_launch"):
+                 "kvq_profile_next_launch", "kv_compress_store_translate"):
         assert want in names
 
 
@@ -164,6 +164,34 @@ def test_compress_argument_checks(kvq):
     assert call(kv=B + 4) == kvq.KVQ_EINVAL
     assert call(score=C + 8) == kvq.KVQ_EINVAL
     assert call(R=-1) == kvq.KVQ_EINVAL
+
+
+def test_compress_translate_argument_checks(kvq):
+    L = kvq.load_library()
+    names = ["layout", "pool", "num_pages", "kv", "score", "ld", "ratio", "pos", "cs", "max_pos",
+             "table", "table_len", "full", "out", "cap", "R", "stream"]
+    ok = (V41, A, 4, B, C, 512, 4, A, B, 10, C, 100, A, B, 16, 5, None)
+
+    def call(**kw):
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return L.kv_compress_store_translate(*[args[n] for n in names])
+    # the compressor's own checks
+    for r in (0, 3, 96, 256):
+        assert call(ratio=r) == kvq.KVQ_ERATIO
+    assert call(layout=0) == kvq.KVQ_ELAYOUT
+    for kw in (dict(kv=None), dict(score=None), dict(pos=None), dict(cs=None), dict(max_pos=0),
+               dict(ld=510), dict(kv=B + 4), dict(R=-1), dict(num_pages=-1)):
+        assert call(**kw) == kvq.KVQ_EINVAL, kw
+    # the translation's checks: more rows than the buffer holds is a capacity refusal
+    assert call(R=17) == kvq.KVQ_ECAPACITY
+    assert call(R=17, table=None, full=None, out=None) == kvq.KVQ_ECAPACITY
+    for kw in (dict(table=None), dict(full=None), dict(out=None), dict(cap=-1),
+               dict(cap=1 << 31), dict(table_len=-1)):
+        assert call(**kw) == kvq.KVQ_EINVAL, kw
+    # nothing to compress and an empty buffer: nothing to do
+    assert call(R=0, cap=0) == kvq.KVQ_OK
+    assert call(R=0, cap=4, out=None) == kvq.KVQ_EINVAL
 
 
 def test_dequant_and_translate_argument_checks(kvq):
