@@ -482,11 +482,11 @@ def trace_summary(results, warmup=10):
         f"# command: {PROFILE_RUNS['trace']}",
         "# (run from the repository root with TMPDIR=/tmp, RESULTS = the results directory;",
         "#  summarised by: python bench.py --write-profiles $RESULTS)",
-        "# The bench launches every kernel on torch's current stream: 30 launches of each step",
-        f"# kernel = {warmup} warmup steps + 10 timed steps + 10 steps of the pass that times the kernels",
-        "# not armed in the timed region.  avg_us covers every launch; after_warmup_us leaves out",
-        f"# the first {warmup} launches of each kernel (the warmup steps, during which the clocks",
-        "# settle), as the bench's own figures do.",
+        "# The bench launches every kernel on torch's current stream: 50 launches of each step",
+        f"# kernel = {warmup} warmup steps + 10 timed steps + 3 passes of 10 steps that time the",
+        "# kernels (plus the mixed step's graph replays).  avg_us covers every launch;",
+        f"# after_warmup_us leaves out the first {warmup} launches of each kernel (the warmup",
+        "# steps, during which the clocks settle), as the bench's own figures do.",
         "",
         f"{'kernel':<52} {'calls':>5} {'avg_us':>10} {'after_warmup_us':>16} {'min_us':>10} {'max_us':>10}",
     ]
@@ -765,12 +765,12 @@ def main():
     # (kv_compress_store_translate) and leaves them in m["loc"] for later consumers
     names = ["compress_mixed_fp4", "dequant_fp4", "compress_c4a", "compress_c128a"]
 
+    # The timed region runs the steps alone, with nothing recorded between the launches.
     # Kernel durations come from events that a kernel's own dispatch records
-    # (kvq_profile_next_launch); each armed launch adds a few microseconds of gap on the
-    # stream, so inside the timed region only C4A and C128A are armed, and the other
-    # kernels' durations come from one more pass of the same steps right after it.  Every
-    # kernel of a timed step is also bracketed by events recorded on the stream (these hold
-    # the gap between commands as well).
+    # (kvq_profile_next_launch) in passes of the same steps right after it; each armed
+    # launch adds a few microseconds of gap on the stream, so one pass arms C4A and C128A
+    # and another the mixed step's kernels.  A third pass brackets every kernel with events
+    # recorded on the stream (these hold the gap between commands as well).
     timed_armed = {2, 3}
 
     def step(k=None, armed=(), clocks=None, ev=None):
@@ -797,17 +797,21 @@ def main():
         step()
     stream_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     clocks = [DispatchTimer(kvq, len(names)) for _ in range(args.steps)]
+    extra = [DispatchTimer(kvq, len(names)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(k, timed_armed, clocks, stream_ev[k])
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    extra = [DispatchTimer(kvq, len(names)) for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(k, timed_armed, clocks)
     other = [j for j in range(len(names)) if j not in timed_armed]
     for k in range(args.steps):
         step(k, other, extra)
+    for k in range(args.steps):
+        step(k, ev=stream_ev[k])
     torch.cuda.synchronize()
     per = {n: [] for n in names}
     per_stream = {n: [] for n in names}
@@ -954,11 +958,12 @@ def main():
         "device": device_facts(torch),
         "mixed_fp4_step_graph": mixed_graph_line,
         "kernels": kernels,
-        "kernel_timing": ("us: HIP events recorded by the kernel's own dispatch (hipExtLaunchKernel), "
-                          "mean over the timed steps for compress_c4a and compress_c128a, and over "
-                          "one more pass of the same steps right after the timed region for the "
-                          "others; us_between_stream_events: events recorded on the stream between "
-                          "the timed launches, which also hold the gap between commands"),
+        "kernel_timing": ("the timed region runs the steps with nothing recorded between launches; "
+                          "us: HIP events recorded by the kernel's own dispatch (hipExtLaunchKernel), "
+                          "mean over a pass of the same steps right after the timed region (one pass "
+                          "for compress_c4a and compress_c128a, one for the mixed step's kernels); "
+                          "us_between_stream_events: a third pass with events recorded on the stream "
+                          "between the launches, which also hold the gap between commands"),
         "copy_1GiB_GB/s": round(copy_gbs, 1),
         "store_configs": stores,
         "micro": micro,
