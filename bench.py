@@ -324,6 +324,32 @@ class DispatchTimer:
         return a.elapsed_time(b) * 1e3
 
 
+def launch_floor(kvq, inputs, cs, reps=20):
+    """The per-launch floor in the step's regime: a library launch that moves almost
+    nothing (kv_store of one row whose slot is outside the pool: it loads the row and
+    stores nothing), armed right after a C4A launch, so that it starts on a busy GPU as
+    the mixed step's kernels do; dispatch-recorded events, median of `reps`."""
+    import numpy as np
+    import torch
+    clock = DispatchTimer(kvq, 1)
+    dev = inputs["c4a"]["kv"].device
+    pool = kvq.new_pool(kvq.V41, 1, dev)
+    k = torch.zeros((1, HEAD), dtype=torch.bfloat16, device=dev)
+    slots = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    d = inputs["c4a"]
+    ts = []
+    for r in range(reps + 2):
+        kvq.kv_compress_store(d["pool"], kvq.V41, d["kv"], d["sc"], d["ratio"], d["pos"], cs, d["slots"])
+        clock.arm(0)
+        kvq.kv_store(pool, kvq.V41, k, slots)
+        if r >= 2:
+            ts.append(clock.us(0))
+    return {"us": round(float(np.median(ts)), 2), "us_p10": round(float(np.percentile(ts, 10)), 2),
+            "us_p90": round(float(np.percentile(ts, 90)), 2),
+            "method": "kv_store of one row with an out-of-pool slot (loads 1 KiB, stores nothing), "
+                      "armed right after a C4A launch; HIP events recorded by its own dispatch, median"}
+
+
 def fp4_configs(kvq, inputs, cs, reps=10):
     """C4A and C128A with the V41_FP4 layout: the same resident inputs, FP4 pools.  Each
     repetition runs C4A then C128A, so every C4A launch follows 8 GiB of other traffic and
@@ -830,6 +856,8 @@ def main():
         fp4 = fp4_configs(kvq, inputs, cs)
         log(f"fp4 configs: c4a {fp4['c4a']['us']} us ({fp4['c4a']['frac_of_peak']}), "
             f"c128a {fp4['c128a']['us']} us ({fp4['c128a']['frac_of_peak']})")
+    floor = launch_floor(kvq, inputs, cs)
+    log(f"launch floor: {floor['us']} us")
 
     # achievable-bandwidth reference (context): a plain 1 GiB device copy
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev).normal_()
@@ -975,6 +1003,7 @@ def main():
         },
         "next_rows": nxt,
         "fp4_configs": fp4,
+        "launch_floor": floor,
         "c4a": {"rows/s": kernels["compress_c4a"]["rows/s"], "GB/s": kernels["compress_c4a"]["GB/s"],
                 "frac_of_peak": kernels["compress_c4a"]["frac_of_peak"]},
         "c128a": {"rows/s": kernels[dom]["rows/s"], "GB/s": kernels[dom]["GB/s"],
