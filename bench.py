@@ -467,15 +467,15 @@ PROFILE_RUNS = {
 }
 SHORT_NAMES = {
     "compress_long_kernel<(kvq::Layout)1, 128": "compress_long<V41, ratio 128> (C128A)",
-    "compress_short_kernel<(kvq::Layout)1, 4>": "compress_short<V41, ratio 4> (C4A)",
-    "compress_short_kernel<(kvq::Layout)2, 4>": "compress_short<V41_FP4, 4> (mixed, translating)",
+    "compress_short_kernel<(kvq::Layout)1, 4, false>": "compress_short<V41, ratio 4> (C4A)",
+    "compress_short_kernel<(kvq::Layout)2, 4, false>": "compress_short<V41_FP4, 4> (mixed, translating)",
     "dequant_kernel<(kvq::Layout)2": "dequant<V41_FP4> (mixed step)",
     "translate_kernel": "translate (three-launch mixed graph)",
     "__amd_rocclr_copyBuffer": "__amd_rocclr_copyBuffer (1 GiB device copy)",
 }
 COPY_KEY = SHORT_NAMES["__amd_rocclr_copyBuffer"]
 DOM_KEY = SHORT_NAMES["compress_long_kernel<(kvq::Layout)1, 128"]
-C4A_KEY = SHORT_NAMES["compress_short_kernel<(kvq::Layout)1, 4>"]
+C4A_KEY = SHORT_NAMES["compress_short_kernel<(kvq::Layout)1, 4, false>"]
 
 
 def _short_name(name):

@@ -12,7 +12,7 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
 C128A = "void kvq::compress_long_kernel<(kvq::Layout)1, 128, 8, 2>(unsigned char*, long)"
-C4A = "void kvq::compress_short_kernel<(kvq::Layout)1, 4>(unsigned char*, long)"
+C4A = "void kvq::compress_short_kernel<(kvq::Layout)1, 4, false>(unsigned char*, long)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
