@@ -224,6 +224,11 @@ def test_empty_inputs_through_the_binding(kvq, cs_small):
         kvq.kv_store_norm_rope(pool, layout, k0, w, 1e-6, i0, cs, i0)
         for ratio in (1, 4, 128):
             kvq.kv_compress_store(pool, layout, f0, f0 if ratio > 1 else None, ratio, i0, cs, i0)
+            loc = torch.full((5,), 7, dtype=torch.int32, device=dev)
+            got = kvq.kv_compress_store_translate(pool, layout, f0, f0, ratio, i0, cs,
+                                                  torch.arange(64, dtype=torch.int32, device=dev), i0, loc)
+            torch.cuda.synchronize()
+            assert got.numel() == 0 and not to_host(loc).any()    # no rows: the buffer is zeroed
         state, count = kvq.new_compress_state(3)
         kvq.kv_compress_state_update(pool, layout, state, count, 4, i0, f0, f0, i0, cs, i0)
         torch.cuda.synchronize()
