@@ -227,12 +227,24 @@ def new_pool(layout, num_pages):
     return np.zeros((num_pages, page_bytes(layout)), np.uint8)
 
 
+def _distinct_stored(slots, num_pages, pos=None, max_pos=None):
+    """Two rows of one call stored at the same slot is a caller error (which row wins is
+    unspecified), so a comparison on such inputs would not be defined: refuse them."""
+    keep = (slots >= 0) & (slots < num_pages * PAGE_ROWS)
+    if pos is not None:
+        keep &= (pos >= 0) & (pos < max_pos)
+    s = slots[keep]
+    if np.unique(s).size != s.size:
+        raise ValueError("duplicate slots among the rows of one call")
+
+
 def kv_store(layout, pool, k_bf16, slots):
     _check(pool, np.uint8, "pool")
     _check(k_bf16, np.uint16, "k")
     _check(slots, np.int32, "slots")
     n = slots.shape[0]
     assert k_bf16.ndim == 2 and k_bf16.shape[0] >= n and k_bf16.shape[1] >= HEAD
+    _distinct_stored(slots, pool.shape[0])
     _ok(lib().orc_kv_store(layout, _p(pool), pool.shape[0], _p(k_bf16), k_bf16.shape[1],
                            _p(slots), n), "kv_store")
 
@@ -245,6 +257,7 @@ def kv_store_rope(layout, pool, k_bf16, pos, cos_sin, slots):
     _check(slots, np.int32, "slots")
     n = slots.shape[0]
     assert pos.shape[0] == n and cos_sin.shape[1] == ROPE_DIM
+    _distinct_stored(slots, pool.shape[0], pos, cos_sin.shape[0])
     _ok(lib().orc_kv_store_rope(layout, _p(pool), pool.shape[0], _p(k_bf16), k_bf16.shape[1],
                                 _p(pos), _p(cos_sin), cos_sin.shape[0], _p(slots), n),
         "kv_store_rope")
@@ -267,6 +280,7 @@ def kv_store_norm_rope(layout, pool, k_bf16, weight_bf16, eps, pos, cos_sin, slo
     _check(slots, np.int32, "slots")
     n = slots.shape[0]
     assert pos.shape[0] == n and weight_bf16.shape == (HEAD,)
+    _distinct_stored(slots, pool.shape[0], pos, cos_sin.shape[0])
     _ok(lib().orc_kv_store_norm_rope(layout, _p(pool), pool.shape[0], _p(k_bf16), k_bf16.shape[1],
                                      _p(weight_bf16), float(eps), _p(pos), _p(cos_sin),
                                      cos_sin.shape[0], _p(slots), n), "kv_store_norm_rope")
@@ -294,6 +308,7 @@ def kv_compress_store(layout, pool, kv, score, ratio, pos, cos_sin, slots):
     _check(slots, np.int32, "slots")
     R = slots.shape[0]
     assert kv.shape == score.shape and kv.shape[0] >= R * ratio and pos.shape[0] == R
+    _distinct_stored(slots, pool.shape[0], pos, cos_sin.shape[0])
     _ok(lib().orc_kv_compress_store(layout, _p(pool), pool.shape[0], _p(kv), _p(score),
                                     kv.shape[1], ratio, _p(pos), _p(cos_sin),
                                     cos_sin.shape[0], _p(slots), R), "kv_compress_store")

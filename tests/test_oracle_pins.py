@@ -856,3 +856,24 @@ def test_dequant_slots_matches_page_dequant(orc, layout):
             assert np.array_equal(out[i], pages[sl])
         else:
             assert np.all(out[i] == 0x1234)
+
+
+def test_duplicate_stored_slots_are_refused(orc):
+    """Two rows of one call stored at the same slot is a caller error; the oracle refuses
+    such inputs (a comparison on them would not be defined), but a duplicate among rows
+    that are skipped (slot outside the pool, position outside the table) is allowed."""
+    import pytest
+    rng = np.random.default_rng(5)
+    k = rng.integers(0, 1 << 15, (4, 512)).astype(np.uint16)
+    cs = np.zeros((8, 64), np.float32)
+    pool = orc.new_pool(orc.V41, 2)
+    with pytest.raises(ValueError):
+        orc.kv_store(orc.V41, pool, k, np.array([3, 7, 3, 9], np.int32))
+    with pytest.raises(ValueError):
+        orc.kv_store_rope(orc.V41, pool, k, np.array([1, 2, 3, 4], np.int32), cs, np.array([5, 5, 6, 7], np.int32))
+    kv = rng.standard_normal((8, 512)).astype(np.float32)
+    with pytest.raises(ValueError):
+        orc.kv_compress_store(orc.V41, pool, kv, kv, 2, np.zeros(4, np.int32), cs, np.array([0, 1, 1, 2], np.int32))
+    # skipped rows may share a slot: out of the pool, or with an out-of-range position
+    orc.kv_store(orc.V41, pool, k, np.array([-1, -1, 200, 200], np.int32))
+    orc.kv_store_rope(orc.V41, pool, k, np.array([1, 9, 9, 2], np.int32), cs, np.array([5, 6, 6, 7], np.int32))
