@@ -1,8 +1,10 @@
 // kvq_kernels.hpp -- gfx950 kernels of the compress -> quantise -> paged-store path.
 //
-// All kernels are HBM-bound streaming kernels (about 1-2 flop and at most 1/4 exp per
-// byte moved), so there is no MFMA here: the design is about wide coalesced loads,
-// enough bytes in flight per CU, and keeping every reduction inside a wavefront.
+// All kernels are HBM-bound streaming kernels (the compressors: one exponential per 8
+// input bytes and about 2 float64 flop per byte moved, against a float64 ridge near 10),
+// so there is no MFMA here: nothing is a contraction.  The design is about wide coalesced
+// loads, enough bytes in flight per CU, each kernel's store policy, and keeping every
+// reduction inside a wavefront.
 #pragma once
 
 #include <hip/hip_runtime.h>
