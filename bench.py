@@ -403,6 +403,25 @@ def ratio_sweep(kvq, wl, dev, cs, kv, sc, c4_pool, c4_slots, reps=5):
         b = bytes_compress(R, r, kvq.bytes_per_token(kvq.V41))
         sweep[f"r{r}"] = {"rows": R, "us": round(us, 1), "GB/s": round(b / us / 1e3, 1),
                           "frac_of_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+    # C4A- and C128A-shaped calls from a few rows (decode-time batches) to the benchmark's
+    # size, each repetition on another region of the 8 GiB input so that it reads cold rows
+    sizes = {}
+    for r, Rs in ((4, (256, 1024, 4096, 16384, 65536)), (128, (64, 256, 1024, 4096, 16384))):
+        for R in Rs:
+            pos = torch.from_numpy(rng.integers(0, 65536, R).astype(np.int32)).to(dev)
+            slots = torch.from_numpy(wl.distinct_slots(rng, R, 64, num_pages * 64)).to(dev)
+            regions = rows_in // (R * r)
+            times = []
+            for k in range(reps + 1):
+                o = (k * 7 % regions) * R * r
+                clock.arm(0)
+                kvq.kv_compress_store(pool, kvq.V41, kv[o:o + R * r], sc[o:o + R * r], r, pos, cs, slots)
+                if k:
+                    times.append(clock.us(0))
+            us = float(np.median(times))
+            b = bytes_compress(R, r, kvq.bytes_per_token(kvq.V41))
+            sizes[f"r{r}_R{R}"] = {"us": round(us, 2), "GB/s": round(b / us / 1e3, 1),
+                                   "frac_of_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
     out = torch.empty((c4_slots.numel(), HEAD), dtype=torch.bfloat16, device=dev)
     times = []
     for k in range(reps + 1):
@@ -443,8 +462,10 @@ def ratio_sweep(kvq, wl, dev, cs, kv, sc, c4_pool, c4_slots, reps=5):
     return {"method": "HIP events recorded by each launch's own dispatch, median of %d launches "
                       "(decode steps: stream events around one full window); the ratio sweep reads the same 8 GiB "
                       "of cold inputs at every ratio; decode steps fold one row per sequence into "
-                      "its 10 KiB float64 state per call (one full window timed)" % reps,
-            "compress_ratio_sweep_v41": sweep, "dequant_slots_c4a_rows": gather,
+                      "its 10 KiB float64 state per call (one full window timed); the size sweep "
+                      "reads another region of the 8 GiB input at each repetition" % reps,
+            "compress_ratio_sweep_v41": sweep, "compress_size_sweep_v41": sizes,
+            "dequant_slots_c4a_rows": gather,
             "compress_state_decode_v41": decode}
 
 
