@@ -91,17 +91,18 @@ int compress_c1(void* pool, int64_t num_pages, const float* kv, int64_t ld, cons
                   slots.table_len, slots.out, slots.cap, R);
 }
 
-// Ratios 2 and 4 store their rows with non-temporal stores when the call reads at least
-// this many bytes: measured on MI355X, plain stores are faster for C4A's 256 MiB of input
-// (whose 8.6 MB of output stays in L2 until the kernel ends) and non-temporal ones 2-3 %
-// faster for 8 GiB; the threshold sits between, at four times the last-level cache.
-constexpr int64_t kShortNtInputBytes = int64_t(1) << 30;
+// Ratios 2 and 4 store their rows with non-temporal stores when the rows written reach
+// the size of the 256 MiB last-level cache, plain stores below.  Measured on MI355X on
+// cold inputs: plain stores are 4-10 % faster from 256 MiB up to 4 GiB of input (up to
+// 138 MB of ratio-4 output, 277 MB at ratio 2 where both are even), non-temporal ones
+// 1-3 % faster at 8 GiB (277 MB of ratio-4 output, 553 MB at ratio 2).
+constexpr int64_t kShortNtOutputBytes = int64_t(256) << 20;
 
 template <Layout L, int kRatio>
 int compress_short(void* pool, int64_t num_pages, const float* kv, const float* score, int64_t ld,
                    const int32_t* pos, const float* cos_sin, int64_t max_pos,
                    kvq::SlotSrc slots, int64_t R, void* stream) {
-    if (R * kRatio * 2 * kvq::kHeadDim * 4 >= kShortNtInputBytes)
+    if (R * kvq::kTokenBytes<L> >= kShortNtOutputBytes)
         return launch(kvq::compress_short_kernel<L, kRatio, true>, dim3(blocks_for(R, kvq::kRowsPerBlock)),
                       dim3(kvq::kWave * kvq::kRowsPerBlock), stream, static_cast<uint8_t*>(pool),
                       num_pages << kvq::kPageBits, kv, score, ld, pos, cos_sin, max_pos, slots.slots, slots.table,
