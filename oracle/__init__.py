@@ -22,7 +22,9 @@ ue8m0             P1 s.1 (exponent from amax bits)          exhaustive vs exact 
 e2m1 / fp4 scale  P1 s.1-2 (e2m1 codes, e4m3 scale per 32)  exhaustive vs brute force
                                                             with exact rational ties
 RoPE              P3 s.3; NeoX half rotation                pos 0 identity; hand-computed
-                                                            angles; norm preservation
+                                                            angles; norm preservation;
+                                                            a worked row whose float32
+                                                            rounding order decides its bf16
 K norm (RMS)      P1 latency table "fused K norm + RoPE"    hand-computed row (eps 0);
                   (formula is a reading)                    power-of-two scale invariance;
                                                             weight channel mapping;
@@ -40,9 +42,11 @@ dequant by slot   P1 s.4 (per-token form)                   equals the matching 
                                                             page dequant; skips out-of-pool
 translate         P2 s.1                                    buffer semantics printed on
                                                             the page (zero tail, refusal)
-whole pipeline    --                                        parity unpinned beyond the
-                                                            pins above (no worked example
-                                                            on the pages)
+composition       P1 s.2-3, P3 s.1-3 (pool, bf16, RoPE,    compress at ratio 1 equals
+                  quantise, store)                          store_rope of the bf16 rows;
+                                                            compress equals the pool then
+                                                            store_rope; norm + RoPE + store
+                                                            equals its parts
 ================  ========================================  ==============================
 """
 import ctypes
