@@ -36,9 +36,11 @@
  *  - Sizes above what one launch covers are refused with KVQ_EINVAL before anything is
  *    enqueued: rows n (or R) <= KVQ_MAX_ROWS, except R <= KVQ_MAX_LONG_ROWS for
  *    compressor ratios of 64 and more; pages P <= KVQ_MAX_PAGES; cap <= 2^31 - 1.
- *  - Inputs must be finite, with |kv| no larger than the largest finite bf16
- *    (about 3.39e38) so that no pooled value rounds to infinity; values outside that
- *    domain give unspecified codes.  fp32 denormals are handled.
+ *  - Inputs must be finite, no larger in magnitude than the largest finite bf16 (about
+ *    3.39e38), and no larger than 2^127 (about 1.7e38) in the last 64 channels, which are
+ *    rotated (a rotated pair can grow by up to a factor sqrt(2)), so that no pooled or
+ *    rotated value overflows; values outside that domain give unspecified codes.  fp32
+ *    denormals are handled.
  *
  * Pool layout (PagedKV, page size 64 tokens, [P1] section 1): the pool is num_pages
  * pages of kvq_page_bytes(layout) bytes each, contiguous from `pool`.  Slot s lives in
@@ -165,7 +167,8 @@ int kv_store_rope_layers(int32_t layout, void* const* pools, int64_t num_pages,
  *   weight     device bf16 bits [512], 16-byte aligned
  *   eps        >= 0 and finite (else KVQ_EINVAL)
  * Other arguments as kv_store_rope.  y equals the correctly rounded value unless the
- * exact quotient lies within a few float64 ulps of a bf16 rounding midpoint. */
+ * exact quotient lies within a few float64 ulps of a bf16 rounding midpoint.  With eps == 0
+ * an all-zero row has no defined value (0 / 0) and its codes are unspecified. */
 int kv_store_norm_rope(int32_t layout, void* pool, int64_t num_pages, const uint16_t* k,
                        int64_t ld, const uint16_t* weight, float eps, const int32_t* pos,
                        const float* cos_sin, int64_t max_pos, const int32_t* slots, int64_t n,
@@ -265,7 +268,8 @@ int kv_dequant_slots(int32_t layout, const void* pool, int64_t num_pages, const 
  *   out[i] = table[full_loc[i]] for i < n (-1 when full_loc[i] is outside
  *            [0, table_len)), out[i] = 0 for n <= i < cap.
  * n > cap returns KVQ_ECAPACITY and enqueues nothing; the caller then translates into a
- * buffer of its own of n entries (the eager, still once-per-step, fallback).
+ * buffer of its own of n entries (the eager, still once-per-step, fallback).  out must
+ * not overlap table or full_loc.
  *   table      device int32[table_len]
  *   full_loc   device int32[n]
  *   out        device int32[cap] */

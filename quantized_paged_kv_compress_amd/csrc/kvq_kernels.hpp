@@ -341,7 +341,7 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_wave_kernel(
 }
 
 // ------------------------------------------------------------------ long-window compressor
-// Large ratios (8..128): one workgroup of kWaves wavefronts per output row.  The window is
+// Ratios 64 and 128: one workgroup of kWaves wavefronts per output row.  The window is
 // cut into chunks of kChunk rows dealt round-robin to the wavefronts (wavefront w folds
 // chunks w, w + kWaves, ...), so the whole workgroup sweeps its window front to back
 // together.  Each wavefront keeps kDepth - 1 chunks in flight while it folds the current
