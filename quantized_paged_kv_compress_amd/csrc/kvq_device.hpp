@@ -445,7 +445,8 @@ __device__ __forceinline__ void rms_norm_row(float (&v)[8], const uint16_t* __re
 // MI355X: non-temporal pays for kernels that read far more than they write over a long
 // run (the long-window compressors) and for the scattered row writers (the multi-layer
 // store, the token gather); a short kernel whose few MB of output can sit in L2 until it
-// ends (C4A) is faster with plain stores.
+// ends (C4A) is faster with plain stores, and the short-window compressors switch to
+// non-temporal stores only once their output outgrows the 256 MiB last-level cache.
 template <bool kNt, typename T>
 __device__ __forceinline__ void put(T* p, T v) {
     if constexpr (kNt)
