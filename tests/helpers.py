@@ -90,6 +90,38 @@ def compare_compressed(got_pool, ref_pool, layout, slots, min_equal=0.999, label
     return frac
 
 
+def code_differs(got_pool, ref_pool, layout, page_ids):
+    """[P*64, 512] mask of the dequant outputs of the listed pages whose code or scale byte
+    differs between two pools (False for page ids outside the pool)."""
+    ids = np.asarray(page_ids, np.int64)
+    valid = (ids >= 0) & (ids < got_pool.shape[0])
+    safe = np.where(valid, ids, 0)
+    cr, sr = CR[layout], SR[layout]
+
+    def parts(pool):
+        pg = pool[safe]
+        codes = pg[:, :64 * cr].reshape(-1, 64, cr)
+        if layout == FP4:
+            codes = np.stack([codes & 15, codes >> 4], axis=-1).reshape(-1, 64, 512)
+        scales = np.repeat(pg[:, 64 * cr:].reshape(-1, 64, sr)[:, :, :16], 32, axis=-1)
+        return codes, scales
+
+    gc, gs = parts(got_pool)
+    rc, rs = parts(ref_pool)
+    return (((gc != rc) | (gs != rs)) & valid[:, None, None]).reshape(-1, 512)
+
+
+def check_step_dequant(orc, layout, ws_host, got_pool, ref_pool, page_ids):
+    """A step's dequant of the GPU's pool against the oracle's dequant of the oracle's pool:
+    equal wherever the two pools hold the same code and scale (everywhere when the
+    compressor's bytes are identical); a code that differs by the one step the compressor
+    rule allows may give another value.  Returns the number of such values."""
+    want = orc.kv_dequant(layout, ref_pool, np.ascontiguousarray(page_ids, np.int32))
+    differs = code_differs(got_pool, ref_pool, layout, page_ids)
+    assert np.array_equal(ws_host[~differs], want[~differs]), "dequant differs where the codes agree"
+    return int(differs.sum())
+
+
 def untouched_equal(got_pool, ref_pool, layout, slots):
     """Every byte outside the rows at `slots` is equal in both pools."""
     mask = np.ones(got_pool.shape, bool)

@@ -10,7 +10,8 @@ kernel), R == 0, the capacity refusal, the benchmark's mixed step, and graph rep
 import numpy as np
 import pytest
 
-from helpers import FP4, V41, compare_compressed, gpu_lib, to_dev, to_host, untouched_equal
+from helpers import (FP4, V41, check_step_dequant, compare_compressed, gpu_lib, to_dev, to_host,
+                     untouched_equal)
 from quantized_paged_kv_compress_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -154,7 +155,7 @@ def test_fused_mixed_fp4_step(kvq, orc, cos_sin, cos_sin_dev):
     orc.kv_compress_store(FP4, ref_pool, d["kv"], d["score"], 4, d["pos"], cos_sin, slots)
     compare_compressed(got_pool, ref_pool, FP4, slots, label="fused mixed fp4")
     assert untouched_equal(got_pool, ref_pool, FP4, slots)
-    assert np.array_equal(to_host(ws), orc.kv_dequant(FP4, got_pool, d["page_ids"]))
+    check_step_dequant(orc, FP4, to_host(ws), got_pool, ref_pool, d["page_ids"])
 
 
 def test_fused_graph_replay_matches_eager(kvq, cos_sin_dev):
