@@ -109,6 +109,17 @@ def graph_us(fn, n_calls, reps=20):
     return float(np.median(times))
 
 
+def evict_caches(buf, mode):
+    """Make the next kernel's inputs cold.  "read": read a 512 MiB buffer, so the caches
+    hold none of the inputs and no dirty lines; "write": fill it, which evicts the inputs
+    too but leaves the last-level cache full of dirty lines that the next kernel then pays
+    to write back (reported beside the read figure as the after-a-large-write regime)."""
+    if mode == "read":
+        buf.sum()
+    else:
+        buf.fill_(1.0)
+
+
 def store_configs(kvq, wl, dev, cs, reps=20, calls=50):
     """The two store workloads at their own sizes: V41 plain store (64 tokens, 16-page pool)
     and V41 store + RoPE (512 tokens, 4096-page pool).  Under 1 MB of data each, so the
@@ -202,32 +213,38 @@ def micro_bench(kvq, wl, dev, cs, layers=61, reps=20, calls=50):
         loc = kvq.kv_translate_slots(tab, full, buf)
         kvq.kv_store_rope_layers(pools, kvq.V41, ks, pos, cs, loc)
 
-    # the one-launch store's own duration (dispatch-recorded events), inputs cold: a 512 MiB
-    # write between repetitions evicts the 32 MB of K rows from the caches
+    # the one-launch store's own duration (dispatch-recorded events), inputs cold: 512 MiB
+    # read (or written) between repetitions evicts the 32 MB of K rows from the caches
     alg = layers * n * (2 * HEAD + 528) + n * (4 + 4 + 256)
     flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
     loc = kvq.kv_translate_slots(tab, full, buf)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(); e1.record()
-    kern = []
-    for r in range(reps + 3):
-        flush.fill_(float(r))
+    kern = {"read": [], "write": []}
+    for r in range(2 * (reps + 3)):
+        mode = ("read", "write")[r % 2]
+        evict_caches(flush, mode)
         kvq.profile_next_launch(e0, e1)
         kvq.kv_store_rope_layers(pools, kvq.V41, ks, pos, cs, loc)
         e1.synchronize()
-        if r >= 3:
-            kern.append(e0.elapsed_time(e1) * 1e3)
+        if r >= 6:
+            kern[mode].append(e0.elapsed_time(e1) * 1e3)
     del flush
-    kus = float(np.median(kern))
+    kus = float(np.median(kern["read"]))
+    kus_w = float(np.median(kern["write"]))
     step = {"layers": layers, "tokens": n,
             "per_layer_translate_us_per_step": round(graph_us(per_layer, 1, reps), 2),
             "hoisted_per_layer_calls_us_per_step": round(graph_us(hoisted_calls, 1, reps), 2),
             "hoisted_one_launch_us_per_step": round(graph_us(hoisted_one_launch, 1, reps), 2),
             "one_launch_kernel_cold": {"us": round(kus, 2), "alg_bytes": alg,
                                        "GB/s": round(alg / (kus * 1e-6) / 1e9, 1),
-                                       "frac_of_peak": round(alg / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+                                       "frac_of_peak": round(alg / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                       "after_512MiB_write_us": round(kus_w, 2),
+                                       "after_512MiB_write_frac_of_peak":
+                                           round(alg / (kus_w * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
             "note": "graph-replayed steps read hot inputs (32 MB of K rows stay in the 256 MB "
-                    "last-level cache); the kernel line reads cold inputs"}
+                    "last-level cache); the kernel line reads cold inputs, evicted by reading 512 MiB "
+                    "(after_512MiB_write: evicted by writing it, which leaves dirty lines to write back)"}
     return {"method": f"HIP graph of {calls} back-to-back launches, median of {reps} replays, "
                       "per-launch microseconds, V41, hot inputs",
             "latency_us": table, "swa_hoisting": step}
@@ -245,13 +262,13 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def mixed_graph(kvq, m, cs, fused=True, reps=20):
+def mixed_graph(kvq, m, cs, fused=True, reps=20, flush_mode="read"):
     """The mixed FP4 step (full -> SWA translation, ratio-4 compress at the translated slots,
     dequant of the touched pages) captured as one HIP graph and replayed; each replay is
-    timed by stream events around it, with a 512 MiB write before it so that its inputs
-    are cold.  fused: the translation runs inside the compressor's launch
-    (kv_compress_store_translate, two launches in all); otherwise kv_translate_slots is a
-    launch of its own (three)."""
+    timed by stream events around it, with 512 MiB read (flush_mode "read") or written
+    ("write") before it so that its inputs are cold.  fused: the translation runs inside
+    the compressor's launch (kv_compress_store_translate, two launches in all); otherwise
+    kv_translate_slots is a launch of its own (three)."""
     import numpy as np
     import torch
 
@@ -277,7 +294,7 @@ def mixed_graph(kvq, m, cs, fused=True, reps=20):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ts = []
     for r in range(reps + 3):
-        flush.fill_(float(r))
+        evict_caches(flush, flush_mode)
         e0.record()
         g.replay()
         e1.record()
@@ -919,15 +936,20 @@ def main():
     mixed_alg = alg["compress_mixed_fp4"] + alg["dequant_fp4"]
     g_us, g_p10, g_p90 = mixed_graph(kvq, m, cs, fused=True)
     s_us, _, _ = mixed_graph(kvq, m, cs, fused=False)
+    w_us, _, _ = mixed_graph(kvq, m, cs, fused=True, flush_mode="write")
     mixed_graph_line = {"us": round(g_us, 2), "us_p10": round(g_p10, 2), "us_p90": round(g_p90, 2),
                   "alg_bytes": mixed_alg, "GB/s": round(mixed_alg / (g_us * 1e-6) / 1e9, 1),
                   "frac_of_peak": round(mixed_alg / (g_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                   "separate_translate_us": round(s_us, 2),
                   "separate_translate_frac_of_peak": round(mixed_alg / (s_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                  "after_512MiB_write_us": round(w_us, 2),
+                  "after_512MiB_write_frac_of_peak": round(mixed_alg / (w_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                   "method": "compress with the translation fused in (kv_compress_store_translate) + dequant "
-                            "replayed as one HIP graph, cold inputs, median of 20 replays timed by stream "
-                            "events around each; separate_translate: the same step with kv_translate_slots "
-                            "as a launch of its own"}
+                            "replayed as one HIP graph, cold inputs (512 MiB read before each replay), "
+                            "median of 20 replays timed by stream events around each; separate_translate: "
+                            "the same step with kv_translate_slots as a launch of its own; "
+                            "after_512MiB_write: inputs evicted by writing 512 MiB instead, which leaves "
+                            "dirty lines in the last-level cache for the step to write back"}
     log(f"mixed step as one graph: {mixed_graph_line['us']} us, {mixed_graph_line['frac_of_peak']} of peak")
     traffic = read_traffic(alg[dom])
 

@@ -258,7 +258,8 @@ int kv_store_rope_layers(int32_t layout, void* const* pools, int64_t num_pages, 
             ptrs.pool[j] = static_cast<uint8_t*>(pools[l0 + j]);
             ptrs.k[j] = k_layers[l0 + j];
         }
-        const dim3 grid(blocks_for(n * cnt, kvq::kRowsPerBlock)), block(kvq::kWave * kvq::kRowsPerBlock);
+        const int64_t groups = (cnt + kvq::kLayersPerWave - 1) / kvq::kLayersPerWave;
+        const dim3 grid(blocks_for(n * groups, kvq::kRowsPerBlock)), block(kvq::kWave * kvq::kRowsPerBlock);
         const int st = layout == KVQ_LAYOUT_V41
                            ? launch(kvq::store_layers_kernel<Layout::V41>, grid, block, stream, ptrs, cnt, nslots,
                                     ld, pos, cos_sin, max_pos, slots, n)
