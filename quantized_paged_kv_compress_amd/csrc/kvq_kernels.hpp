@@ -60,7 +60,8 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void store_kernel(
 // consecutive wavefronts stream consecutive rows of the same layers.  Measured on MI355X
 // at 61 layers x 512 tokens with cold, clean caches: 4 layers per wavefront is 9-12 %
 // faster than 1 (fewer wavefronts, each with more loads in flight), 2 and 8 are slower
-// than 4; non-temporal row stores are 1-6 % faster than plain ones.
+// than 4, and so are workgroups of 1, 2 or 8 wavefronts.  Non-temporal row stores: 2-4 %
+// faster than plain ones right after a large write, 2-3 % slower with clean caches.
 constexpr int kMaxLayers = 64;
 constexpr int kLayersPerWave = 4;
 
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(kWave * kRowsPerBlock) void compress_wave_kernel(
 // rotates, quantises and stores the row.  Measured on MI355X: ratio 128 is fastest with 4
 // wavefronts, 1-row chunks and 2 chunks in flight, ratio 64 with 2 wavefronts, 2-row
 // chunks and 2 in flight; 8 wavefronts per row run 10-20 % slower with float64 pooling.
-// The row is written with non-temporal stores: 3-4 % faster than plain ones at both ratios.
+// The row is written with non-temporal stores: 2-5 % faster than plain ones at both ratios.
 // This lane's 8 channels (two-half mapping) of a channel-indexed row held in LDS.
 __device__ __forceinline__ void load_lds_f32x8(const float* row, int lane, float (&v)[8]) {
 #pragma unroll
