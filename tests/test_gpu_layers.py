@@ -53,10 +53,11 @@ def test_hoisted_step_61_layers(kvq, orc, layout):
     check_layers(kvq, orc, layout, pools, ks, pos, cs, table[full])
 
 
-@pytest.mark.parametrize("L,n", [(1, 1), (2, 77), (64, 33), (65, 130), (130, 5)])
+@pytest.mark.parametrize("L,n", [(1, 1), (2, 77), (3, 9), (4, 64), (7, 3), (64, 33), (65, 130), (130, 5)])
 def test_layer_counts_strides_and_skipped_rows(kvq, orc, L, n):
-    """Layer counts across the 64-per-launch boundary, ragged rows, a row stride above 512,
-    and rows skipped for out-of-pool slots and out-of-range positions."""
+    """Layer counts across the 64-per-launch boundary and the 4-layer groups of a
+    wavefront, ragged rows, a row stride above 512, and rows skipped for out-of-pool slots
+    and out-of-range positions."""
     rng = np.random.default_rng(1000 + L * 7 + n)
     num_pages, ld, max_pos = 4, 640, 3000
     cs = np.ascontiguousarray(wl.rope_cos_sin()[:max_pos])
