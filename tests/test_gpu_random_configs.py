@@ -15,6 +15,8 @@ fp32 denormals, magnitudes near 1e38, equal scores (the window mean; with bf16 i
 ratio 2 the mean of two neighbours is an exact bf16 midpoint), one dominant score per
 window, windows of exact zeros, and rows that cancel.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -25,8 +27,9 @@ pytestmark = pytest.mark.gpu
 RATIOS = (1, 2, 4, 8, 16, 32, 64, 128)
 FAMILIES = ("normal", "channel_scales", "denormal", "large", "equal_scores", "dominant",
             "zeros", "cancel", "midpoints")
-N_COMPRESS = 64
-N_STORE = 24
+# KVQ_RANDOM_CASES widens the sweep (more seeds of both kinds) for a longer numerics run
+N_COMPRESS = int(os.environ.get("KVQ_RANDOM_CASES", 64))
+N_STORE = max(24, N_COMPRESS * 3 // 8)
 CANARY8 = 0xA5
 CANARY16 = 0x5A5A
 
