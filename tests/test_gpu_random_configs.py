@@ -8,7 +8,8 @@ pool is canary-filled and compared with the oracle's (compressor rule on the sto
 every other byte equal), and the translated buffer bit for bit.  The oracle's pool is
 then dequantised on the GPU, page list with ids outside the pool included, and compared
 with the oracle's dequant bit for bit.  The store cases do the same for kv_store,
-kv_store_rope and kv_store_norm_rope.
+kv_store_rope and kv_store_norm_rope, and the decode-state cases fold rows of the same
+value families one call at a time (kv_compress_state_update) against the batch oracle.
 
 Value families beyond the benchmark's normal rows: per-channel scales spread over 2^+-60,
 fp32 denormals, magnitudes near 1e38, equal scores (the window mean; with bf16 inputs at
@@ -230,3 +231,79 @@ def test_random_store_config(kvq, orc, seed):
     else:
         assert np.array_equal(got, ref), f"{int((got != ref).sum())} pool bytes differ"
     dequant_check(kvq, orc, layout, ref, np.unique(stored >> 6), rng)
+
+
+N_STATE = max(24, N_COMPRESS * 3 // 8)
+
+
+def draw_state(seed):
+    rng = np.random.default_rng(7500 + seed)
+    layout = (V41, FP4)[seed % 2]
+    ratio = int(rng.choice([1, 2, 3, 4, 7, 16, 64, 128, 200]))
+    S = int(rng.integers(1, 300))
+    T = int(rng.integers(1, 3 * ratio + 3))
+    family = FAMILIES[int(rng.integers(0, len(FAMILIES)))]
+    return rng, dict(layout=layout, ratio=ratio, S=S, T=T, family=family)
+
+
+@pytest.mark.parametrize("seed", range(N_STATE))
+def test_random_state_config(kvq, orc, seed):
+    """The decode-step state: S sequences join at random steps and add one row per call in a
+    shuffled order, rows drawn from a value family; every completed window must equal the
+    batch compressor on the same rows, incomplete windows store nothing, a few windows end
+    at slots outside the pool, and the counts end at (rows seen) mod ratio."""
+    import torch
+    rng, c = draw_state(seed)
+    log(f"[random state {seed}] {c}")
+    layout, ratio, S, T = c["layout"], c["ratio"], c["S"], c["T"]
+    num_pages, max_pos = 64, 65536
+    nslots = num_pages * 64
+    cs = wl.rope_cos_sin()
+    t0 = rng.integers(0, max(1, T // 3), S)
+    nrows = np.maximum(T - t0, 0)
+    nwin = nrows // ratio
+    rows, scs = [], []
+    for s_ in range(S):
+        x, sc_ = family_values(rng, c["family"], (nwin[s_] + 1) * ratio, ratio, 512)
+        rows.append(np.ascontiguousarray(x[:nrows[s_]]))
+        scs.append(np.ascontiguousarray(sc_[:nrows[s_]]))
+    wslots = (rng.choice(nslots + 16, int(nwin.sum()) + S, replace=False) - 8).astype(np.int32)
+    win_slot, win_pos, k_ = [], [], 0
+    for s_ in range(S):
+        win_slot.append(wslots[k_:k_ + nwin[s_] + 1])
+        k_ += nwin[s_] + 1
+        win_pos.append(rng.integers(0, max_pos, nwin[s_] + 1).astype(np.int32))
+    pool = kvq.new_pool(layout, num_pages)
+    pool.fill_(CANARY8)
+    state, count = kvq.new_compress_state(S + 5)
+    sid_of = rng.permutation(S + 5)[:S].astype(np.int32)
+    cs_d = to_dev(cs)
+    for t in range(T):
+        act = [s_ for s_ in range(S) if t >= t0[s_]]
+        if not act:
+            continue
+        rng.shuffle(act)
+        r_idx = [t - t0[s_] for s_ in act]
+        kv = np.stack([rows[s_][r] for s_, r in zip(act, r_idx)])
+        sc = np.stack([scs[s_][r] for s_, r in zip(act, r_idx)])
+        w_idx = [r // ratio for r in r_idx]
+        pos = np.array([win_pos[s_][w] for s_, w in zip(act, w_idx)], np.int32)
+        slots = np.array([win_slot[s_][w] for s_, w in zip(act, w_idx)], np.int32)
+        kvq.kv_compress_state_update(pool, layout, state, count, ratio, to_dev(sid_of[act]), to_dev(kv),
+                                     to_dev(sc), to_dev(pos), cs_d, to_dev(slots))
+    torch.cuda.synchronize()
+    got = to_host(pool)
+    assert np.array_equal(to_host(count)[sid_of], (nrows % ratio).astype(np.int32)), "counts"
+    ref = np.full((num_pages, orc.page_bytes(layout)), CANARY8, np.uint8)
+    stored = []
+    for s_ in range(S):
+        if nwin[s_] == 0:
+            continue
+        sl = np.ascontiguousarray(win_slot[s_][:nwin[s_]])
+        orc.kv_compress_store(layout, ref, np.ascontiguousarray(rows[s_][:nwin[s_] * ratio]),
+                              np.ascontiguousarray(scs[s_][:nwin[s_] * ratio]), ratio,
+                              np.ascontiguousarray(win_pos[s_][:nwin[s_]]), cs, sl)
+        stored.append(sl[(sl >= 0) & (sl < nslots)])
+    stored = np.concatenate(stored) if stored else np.zeros(0, np.int32)
+    compare_compressed(got, ref, layout, stored, label=f"random state {seed}")
+    assert untouched_equal(got, ref, layout, stored), "bytes outside the completed windows"
